@@ -1,0 +1,308 @@
+// Batched decode of the Gated DeltaNet layer on gfx950: one token per row.
+//
+//   conv_update_kernel  slot-indexed conv window shift + depthwise conv + SiLU
+//                       over the fused [q|k|v] channels (pegainfer PR #1003,
+//                       PR body: the "GDR decode/conv" chain on slot-indexed
+//                       conv state).
+//   decode_kernel       per (row, V-head): l2norm of q/k, softplus gates, one
+//                       read-modify-write pass over the f32 state tile
+//                       S[dk][dv], and the gated RMSNorm epilogue (pegainfer
+//                       issue #1001, Splits, "Batched eager TP decode": one
+//                       batched launch over all decode rows).
+//
+// The state update reads S once: with kappa = S^T k and rho = S^T q taken from
+// the old state,
+//   u  = beta (v - e^g kappa),   S' = e^g S + k u^T,   o = S'^T q = e^g rho + u (k.q)
+// so the kernel is one coalesced f32 read and one write of the tile, the
+// bandwidth floor of the step.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// ------------------------------------------------------------- conv update
+
+struct ConvParams {
+  const void* x;        // [B][C] act
+  const void* weight;   // [C][K] act
+  void* pool;           // [P][K][C] act
+  float* out;           // [B][C] f32
+  const int32_t* slot_idx;
+  int B, C, num_slots;
+};
+
+// One thread owns four consecutive channels of one row; K taps per channel.
+template <typename Act, int K>
+__global__ __launch_bounds__(256) void conv_update_kernel(ConvParams p) {
+  using io = act_io<Act>;
+  const int row = blockIdx.y;
+  const int ch = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (ch >= p.C) return;
+  const int slot = p.slot_idx[row];
+  float* out = p.out + (size_t)row * p.C + ch;
+  if (slot < 0 || slot >= p.num_slots) {
+    *reinterpret_cast<f32x4*>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  void* win = static_cast<char*>(p.pool) + (size_t)slot * K * p.C * io::bytes;
+  f32x4 col[K];
+#pragma unroll
+  for (int j = 1; j < K; ++j) col[j - 1] = io::load4(win, (size_t)j * p.C + ch);
+  col[K - 1] = io::load4(p.x, (size_t)row * p.C + ch);
+  float wt[4][K];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < K; ++j) wt[c][j] = io::load(p.weight, (size_t)(ch + c) * K + j);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    acc.x = fmaf(wt[0][j], col[j].x, acc.x);
+    acc.y = fmaf(wt[1][j], col[j].y, acc.y);
+    acc.z = fmaf(wt[2][j], col[j].z, acc.z);
+    acc.w = fmaf(wt[3][j], col[j].w, acc.w);
+  }
+  f32x4 r = {silu(acc.x), silu(acc.y), silu(acc.z), silu(acc.w)};
+  *reinterpret_cast<f32x4*>(out) = r;
+  // the window stores raw inputs, so re-storing them is lossless
+#pragma unroll
+  for (int j = 0; j < K; ++j) io::store4(win, (size_t)j * p.C + ch, col[j]);
+}
+
+// ------------------------------------------------------------- state step
+
+struct DecodeParams {
+  const float* qkv;     // [B][C] f32
+  const void* z;        // [B][Hv][dv] act
+  const void* a;        // [B][Hv] act
+  const void* b;        // [B][Hv] act
+  void* y;              // [B][Hv][dv] act
+  float* o_raw;         // [B][Hv][dv] f32 or null
+  float* rec;           // [P][Hv][D][D] f32
+  const int32_t* slot_idx;
+  const float* A_log;
+  const float* dt_bias;
+  const float* norm_w;
+  int B, Hk, Hv, C, num_slots, r;
+  float l2eps, rmseps, scale;
+};
+
+// One workgroup per (row, V-head).  Thread t owns the four state columns
+// 4*(t % CG) .. +3 of rows (t / CG) + RG*i: each wave instruction moves whole
+// contiguous rows, and the whole tile is requested before any arithmetic.
+template <typename Act, int D, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
+  using io = act_io<Act>;
+  constexpr int CG = D / 4;         // column groups of four floats
+  constexpr int RG = NT / CG;       // row groups
+  constexpr int RPT = D / RG;       // rows per thread
+  constexpr int NW = NT / 64;       // waves
+  constexpr int QKV_PER = (3 * D + NT - 1) / NT;
+  static_assert(NT % CG == 0 && D % RG == 0 && CG <= 64 && NT % 64 == 0, "layout");
+
+  __shared__ float s_qkv[3 * D];
+  __shared__ f32x4 s_red[NW][2][CG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cg = tid % CG, rg = tid / CG;
+  const int row = blockIdx.x / p.Hv;
+  const int h = blockIdx.x - row * p.Hv;
+  const size_t out_off = ((size_t)row * p.Hv + h) * D;
+  const int slot = p.slot_idx[row];
+  if (slot < 0 || slot >= p.num_slots) {  // padding row: zeros, no state access
+    for (int j = tid; j < D; j += NT) {
+      io::store(p.y, out_off + j, 0.f);
+      if (p.o_raw) p.o_raw[out_off + j] = 0.f;
+    }
+    return;
+  }
+  const int m = h / p.r;  // K-head read by V-head h (repeat_interleave)
+
+  // q, k (K-head m) and v (V-head h): issued before the state tile
+  const float* xr = p.qkv + (size_t)row * p.C;
+  float tmp[QKV_PER];
+#pragma unroll
+  for (int e = 0; e < QKV_PER; ++e) {
+    const int j = tid + e * NT;
+    if (j < 3 * D) {
+      const int part = j / D, jj = j - part * D;
+      const size_t off = part == 0 ? (size_t)m * D + jj
+                       : part == 1 ? (size_t)(p.Hk + m) * D + jj
+                                   : (size_t)2 * p.Hk * D + (size_t)h * D + jj;
+      tmp[e] = xr[off];
+    }
+  }
+  float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
+  f32x4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg + RG * i) * D + 4 * cg);
+
+  float g, beta;
+  gates(p.A_log[h], p.dt_bias[h], io::load(p.a, (size_t)row * p.Hv + h),
+        io::load(p.b, (size_t)row * p.Hv + h), g, beta);
+  const float eg = expf(g);
+
+#pragma unroll
+  for (int e = 0; e < QKV_PER; ++e) {
+    const int j = tid + e * NT;
+    if (j < 3 * D) s_qkv[j] = tmp[e];
+  }
+  __syncthreads();
+
+  // l2 norms and k.q, every wave on its own (no second barrier)
+  float sqq = 0.f, skk = 0.f, sqk = 0.f;
+  for (int j = lane; j < D; j += 64) {
+    const float qv = s_qkv[j], kv = s_qkv[D + j];
+    sqq = fmaf(qv, qv, sqq);
+    skk = fmaf(kv, kv, skk);
+    sqk = fmaf(qv, kv, sqk);
+  }
+  sqq = wave_sum(sqq);
+  skk = wave_sum(skk);
+  sqk = wave_sum(sqk);
+  const float rq = p.scale / sqrtf(sqq + p.l2eps);
+  const float rk = 1.0f / sqrtf(skk + p.l2eps);
+  const float kq = sqk * rq * rk;  // k_hat . q_hat
+
+  // kappa = S^T k_hat, rho = S^T q_hat over this thread's rows
+  f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r_ = rg + RG * i;
+    const float kk = s_qkv[D + r_] * rk, qq = s_qkv[r_] * rq;
+    kap += s[i] * kk;
+    rho += s[i] * qq;
+  }
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1) {
+    kap.x += __shfl_xor(kap.x, off, 64); kap.y += __shfl_xor(kap.y, off, 64);
+    kap.z += __shfl_xor(kap.z, off, 64); kap.w += __shfl_xor(kap.w, off, 64);
+    rho.x += __shfl_xor(rho.x, off, 64); rho.y += __shfl_xor(rho.y, off, 64);
+    rho.z += __shfl_xor(rho.z, off, 64); rho.w += __shfl_xor(rho.w, off, 64);
+  }
+  if (lane < CG) {
+    s_red[wave][0][cg] = kap;
+    s_red[wave][1][cg] = rho;
+  }
+  __syncthreads();
+  kap = s_red[0][0][cg];
+  rho = s_red[0][1][cg];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    kap += s_red[w][0][cg];
+    rho += s_red[w][1][cg];
+  }
+
+  const f32x4 v = *reinterpret_cast<const f32x4*>(&s_qkv[2 * D + 4 * cg]);
+  const f32x4 u = beta * (v - eg * kap);
+  const f32x4 o = eg * rho + u * kq;
+
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r_ = rg + RG * i;
+    const float kk = s_qkv[D + r_] * rk;
+    f32x4 ns;
+    ns.x = fmaf(eg, s[i].x, kk * u.x);
+    ns.y = fmaf(eg, s[i].y, kk * u.y);
+    ns.z = fmaf(eg, s[i].z, kk * u.z);
+    ns.w = fmaf(eg, s[i].w, kk * u.w);
+    *reinterpret_cast<f32x4*>(S + (size_t)r_ * D + 4 * cg) = ns;
+  }
+
+  // gated RMSNorm over the D outputs of this head (wave 0; every row group
+  // of the wave holds all columns, so the xor-reduction over the CG lanes of
+  // a group yields the full sum)
+  if (wave == 0) {
+    float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+    for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
+    if (lane < CG) {
+      const f32x4 nw = *reinterpret_cast<const f32x4*>(p.norm_w + 4 * cg);
+      const f32x4 zz = io::load4(p.z, out_off + 4 * cg);
+      f32x4 yv;
+      yv.x = nw.x * o.x * inv * silu(zz.x);
+      yv.y = nw.y * o.y * inv * silu(zz.y);
+      yv.z = nw.z * o.z * inv * silu(zz.z);
+      yv.w = nw.w * o.w * inv * silu(zz.w);
+      io::store4(p.y, out_off + 4 * cg, yv);
+      if (p.o_raw) *reinterpret_cast<f32x4*>(p.o_raw + out_off + 4 * cg) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------- launchers
+
+template <typename Act>
+static hipError_t conv_dispatch(const ConvParams& p, int K, hipStream_t st) {
+  dim3 grid((p.C / 4 + 255) / 256, p.B);
+  switch (K) {
+    case 2: conv_update_kernel<Act, 2><<<grid, 256, 0, st>>>(p); break;
+    case 3: conv_update_kernel<Act, 3><<<grid, 256, 0, st>>>(p); break;
+    case 4: conv_update_kernel<Act, 4><<<grid, 256, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_update(const gdn_geometry& g, const gdn_layer_weights& w,
+                              const gdn_state_pool& pool, const int32_t* slot_idx,
+                              int B, const void* qkv_in, float* qkv_out,
+                              hipStream_t stream) {
+  ConvParams p;
+  p.x = qkv_in;
+  p.weight = w.conv_weight;
+  p.pool = pool.conv;
+  p.out = qkv_out;
+  p.slot_idx = slot_idx;
+  p.B = B;
+  p.C = 2 * g.num_k_heads * g.head_k_dim + g.num_v_heads * g.head_v_dim;
+  p.num_slots = pool.num_slots;
+  if (g.act_dtype == GDN_BF16) return conv_dispatch<__bf16>(p, g.conv_kernel, stream);
+  return conv_dispatch<float>(p, g.conv_kernel, stream);
+}
+
+template <typename Act>
+static hipError_t decode_dispatch(const DecodeParams& p, int D, hipStream_t st) {
+  dim3 grid(p.B * p.Hv);
+  switch (D) {
+    case 32: decode_kernel<Act, 32, 64><<<grid, 64, 0, st>>>(p); break;
+    case 64: decode_kernel<Act, 64, 128><<<grid, 128, 0, st>>>(p); break;
+    case 128: decode_kernel<Act, 128, 256><<<grid, 256, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const gdn_geometry& g, const gdn_layer_weights& w,
+                         const gdn_state_pool& pool, const int32_t* slot_idx, int B,
+                         const float* qkv, const void* z, const void* a,
+                         const void* b, void* y, float* o_raw, hipStream_t stream) {
+  DecodeParams p;
+  p.qkv = qkv;
+  p.z = z;
+  p.a = a;
+  p.b = b;
+  p.y = y;
+  p.o_raw = o_raw;
+  p.rec = pool.recurrent;
+  p.slot_idx = slot_idx;
+  p.A_log = w.A_log;
+  p.dt_bias = w.dt_bias;
+  p.norm_w = w.norm_weight;
+  p.B = B;
+  p.Hk = g.num_k_heads;
+  p.Hv = g.num_v_heads;
+  p.C = 2 * g.num_k_heads * g.head_k_dim + g.num_v_heads * g.head_v_dim;
+  p.num_slots = pool.num_slots;
+  p.r = g.num_v_heads / g.num_k_heads;
+  p.l2eps = g.l2norm_eps;
+  p.rmseps = g.rmsnorm_eps;
+  p.scale = g.scale > 0.f ? g.scale : 1.0f / sqrtf((float)g.head_k_dim);
+  if (g.act_dtype == GDN_BF16) return decode_dispatch<__bf16>(p, g.head_k_dim, stream);
+  return decode_dispatch<float>(p, g.head_k_dim, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,37 @@
+// Host-side launchers of the libgdn kernels.  Arguments have been validated
+// by the C ABI layer (abi.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+hipError_t launch_conv_update(const gdn_geometry& g, const gdn_layer_weights& w,
+                              const gdn_state_pool& pool, const int32_t* slot_idx,
+                              int B, const void* qkv_in, float* qkv_out,
+                              hipStream_t stream);
+
+hipError_t launch_decode(const gdn_geometry& g, const gdn_layer_weights& w,
+                         const gdn_state_pool& pool, const int32_t* slot_idx, int B,
+                         const float* qkv, const void* z, const void* a,
+                         const void* b, void* y, float* o_raw, hipStream_t stream);
+
+// Token-indexed scratch layout of the chunkwise prefill (see prefill.hip).
+size_t prefill_scratch_bytes(const gdn_geometry& g, long long total_tokens,
+                             long long num_seqs);
+
+hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
+                          const gdn_state_pool& pool, const int32_t* cu_seqlens,
+                          int max_len, long long total_tokens,
+                          const int32_t* slot_idx, const uint8_t* has_init, int N,
+                          const void* qkv_in, const void* z, const void* a,
+                          const void* b, void* y, float* o_raw, void* scratch,
+                          hipStream_t stream);
+
+hipError_t launch_compact(const gdn_geometry& g, const gdn_state_pool* pools, int L,
+                          const int32_t* src, const int32_t* dst, int n,
+                          hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,177 @@
+"""GPU parity of chunkwise prefill (gdn_prefill_chunked) against the f64
+oracle, through the C ABI: ragged and packed sequences, the tiny f32 layer
+(prefill then decode), the rank-local 4096-token prefill and the packed
+varlen prefill at full head count."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import (TOL_F32, Layer, Pool, assert_close, decode_step, host,
+                         maxrel_heads, maxrel_states, prefill, y_tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_prefill(L, rec, conv, cu, slots, d, has_init=None, heads=None):
+    """Oracle of a packed prefill on a pool; with `heads` only those V-heads
+    are computed (states of other heads are then not meaningful)."""
+    S = rec.astype(np.float64)
+    W = conv.astype(np.float64)
+    if heads is None:
+        y, o = oracle.pool_run(L.og, L.ow, S, W, cu, slots, d["x"], d["z"], d["a"], d["b"],
+                               has_init=has_init)
+        return y, o, S, W
+    N = len(cu) - 1
+    S0 = np.stack([S[s] if (has_init is None or has_init[n]) else np.zeros_like(S[0])
+                   for n, s in enumerate(slots)])
+    W0 = np.stack([W[s] if (has_init is None or has_init[n]) else np.zeros_like(W[0])
+                   for n, s in enumerate(slots)])
+    mask = np.zeros(L.s.num_v_heads, np.uint8)
+    mask[list(heads)] = 1
+    y, o, Sn, Wn = oracle.sequences(L.og, L.ow, cu, d["x"], d["z"], d["a"], d["b"], S0, W0,
+                                    head_mask=mask)
+    for n, s in enumerate(slots):
+        S[s] = Sn[n]
+        W[s] = Wn[n]
+    return y, o, S, W
+
+
+def _check_prefill(s, w, rec, conv, cu, slots, d, has_init=None, heads=None, tag=""):
+    print(f"[prefill] {tag} T={int(cu[-1])} N={len(cu) - 1}", flush=True)
+    L = Layer(s, w)
+    P = Pool(s, rec, conv)
+    y, o = prefill(L, P, cu, slots, d["x"], d["z"], d["a"], d["b"], has_init=has_init)
+    torch.cuda.synchronize()
+    yo, oo, S, W = _oracle_prefill(L, rec, conv, cu, slots, d, has_init, heads)
+    hs = np.arange(s.num_v_heads) if heads is None else np.asarray(heads)
+    yh, oh = host(y), host(o)
+    live = np.asarray([sl for sl in slots if sl >= 0])
+    tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
+                          if slots[n] >= 0] + [np.zeros(0, np.int64)]).astype(np.int64)
+    if tok.size:
+        assert_close("y", maxrel_heads(yh[tok][:, hs], yo[tok][:, hs]), y_tol(s))
+        assert_close("o_raw", maxrel_heads(oh[tok][:, hs], oo[tok][:, hs]), TOL_F32)
+    rec_gpu, conv_gpu = host(P.rec), host(P.conv)
+    if live.size:
+        assert_close("state", maxrel_states(rec_gpu[live][:, hs], S[live][:, hs]), TOL_F32)
+        np.testing.assert_array_equal(conv_gpu[live], W[live])
+    pad_tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
+                              if slots[n] < 0] + [np.zeros(0, np.int64)]).astype(np.int64)
+    assert not yh[pad_tok].any() and not oh[pad_tok].any()
+    untouched = np.setdiff1d(np.arange(rec.shape[0]), live)
+    np.testing.assert_array_equal(rec_gpu[untouched], rec[untouched])
+    np.testing.assert_array_equal(conv_gpu[untouched], conv[untouched])
+    return L, P, y, o
+
+
+def _packed(seed, s, lens, P, slow=False):
+    rng = np.random.default_rng(seed)
+    w = wl.layer_weights(rng, s, slow)
+    rec, conv = wl.state_pool(rng, s, P)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = wl.token_inputs(rng, s, int(cu[-1]))
+    return w, rec, conv, cu, d
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 63, 64, 65, 130, 200])
+def test_prefill_ragged_single(T):
+    s = wl.Shape(2, 4, 32, 32, 4, "f32")
+    w, rec, conv, cu, d = _packed(100 + T, s, [T], 2)
+    _check_prefill(s, w, rec, conv, cu, np.array([1], np.int32), d, tag=f"f32 d32 T={T}")
+
+
+def test_prefill_packed_mixed_bf16():
+    """Packed sequences with a zero-length one, a fresh start (has_init = 0),
+    a padding sequence (slot -1) and partial last chunks."""
+    s = wl.Shape(4, 8, 64, 64, 4, "bf16")
+    lens = [70, 0, 3, 129, 64, 17]
+    slots = np.array([4, 0, 7, -1, 2, 5], np.int32)
+    init = np.array([1, 1, 0, 1, 0, 1], np.uint8)
+    w, rec, conv, cu, d = _packed(200, s, lens, 9)
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="packed bf16 d64")
+
+
+@pytest.mark.parametrize("K", [2, 3])
+def test_prefill_conv_widths(K):
+    s = wl.Shape(2, 4, 32, 32, K, "bf16")
+    w, rec, conv, cu, d = _packed(300 + K, s, [2, 90], 3)
+    _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"K={K}")
+
+
+def test_prefill_slow_decay_long_carry():
+    """Slow decay (e^g ~ 0.98..0.998) so the state carries across many chunks."""
+    s = wl.RANK_LOCAL
+    w, rec, conv, cu, d = _packed(400, s, [700], 1, slow=True)
+    _check_prefill(s, w, rec, conv, cu, np.array([0], np.int32), d, tag="slow decay d128")
+
+
+def test_tiny_prefill_then_decode_f32():
+    """Tiny f32 layer: a 64-token prefill then 8 decode steps, against the
+    oracle, and against one 72-token prefill on the GPU."""
+    work = wl.tiny(seed=0)
+    s, d = work.shape, work.data
+    L = Layer(s, d["weights"])
+    P = Pool(s, d["rec"], d["conv"])
+    pre = d["prefill"]
+    y, o = prefill(L, P, d["cu_seqlens"], d["slot_idx"], pre["x"], pre["z"], pre["a"], pre["b"])
+    S, W = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
+    yo, oo = oracle.pool_run(L.og, L.ow, S, W, d["cu_seqlens"], d["slot_idx"], pre["x"],
+                             pre["z"], pre["a"], pre["b"])
+    assert_close("prefill y", maxrel_heads(host(y), yo), TOL_F32)
+    assert_close("prefill o", maxrel_heads(host(o), oo), TOL_F32)
+    ys = [host(y)]
+    for step in d["steps"]:
+        yd, od = decode_step(L, P, d["slot_idx"], step["x"], step["z"], step["a"], step["b"])
+        yo, oo = oracle.pool_run(L.og, L.ow, S, W, [0, 1], d["slot_idx"], step["x"], step["z"],
+                                 step["a"], step["b"])
+        assert_close("decode y", maxrel_heads(host(yd), yo), TOL_F32)
+        ys.append(host(yd))
+    assert_close("state", maxrel_states(host(P.rec), S), TOL_F32)
+    np.testing.assert_array_equal(host(P.conv), W)
+    # the same 72 tokens as one prefill on a fresh pool
+    cat = {k: np.concatenate([pre[k]] + [st[k] for st in d["steps"]]) for k in pre}
+    P2 = Pool(s, d["rec"], d["conv"])
+    y72, _ = prefill(L, P2, [0, 72], [0], cat["x"], cat["z"], cat["a"], cat["b"])
+    assert_close("prefill(72) vs prefill(64)+8 decode",
+                 maxrel_heads(host(y72), np.concatenate(ys)), TOL_F32)
+    assert_close("state handoff", maxrel_states(host(P2.rec), host(P.rec)), TOL_F32)
+
+
+def test_prefill_rank_local_t4096():
+    """One 4096-token sequence, Hk=8, Hv=16, d=128, bf16, N(0, 0.1) initial
+    state; every head checked."""
+    work = wl.prefill_single(seed=0)
+    d = work.data
+    _check_prefill(work.shape, d["weights"], d["rec"], d["conv"], d["cu_seqlens"],
+                   d["slot_idx"], d, has_init=d["has_init"], tag=work.name)
+
+
+def test_prefill_varlen8_full_heads_sampled():
+    """Eight packed sequences of U(128, 8192) tokens at Hk=16, Hv=32, d=128,
+    per-sequence nonzero initial states; four V-heads (two sibling pairs)
+    checked against the oracle, conv windows of all channels checked."""
+    work = wl.prefill_varlen(seed=0)
+    d = work.data
+    _check_prefill(work.shape, d["weights"], d["rec"], d["conv"], d["cu_seqlens"],
+                   d["slot_idx"], d, has_init=d["has_init"], heads=[0, 1, 17, 30],
+                   tag=work.name)
+
+
+def test_prefill_equals_decode_steps():
+    """Property at any size: a prefill of T tokens equals T decode steps."""
+    s = wl.RANK_LOCAL
+    w, rec, conv, cu, d = _packed(500, s, [150], 2)
+    L = Layer(s, w)
+    Pa = Pool(s, rec, conv)
+    ya, _ = prefill(L, Pa, cu, [1], d["x"], d["z"], d["a"], d["b"])
+    Pb = Pool(s, rec, conv)
+    ys = []
+    for t in range(150):
+        yt, _ = decode_step(L, Pb, [1], d["x"][t:t + 1], d["z"][t:t + 1], d["a"][t:t + 1],
+                            d["b"][t:t + 1], want_o=False)
+        ys.append(host(yt))
+    assert_close("y", maxrel_heads(host(ya), np.concatenate(ys)), y_tol(s))
+    assert_close("state", maxrel_states(host(Pa.rec)[1], host(Pb.rec)[1]), TOL_F32)
+    np.testing.assert_array_equal(host(Pa.conv), host(Pb.conv))

@@ -172,8 +172,9 @@ def prefill_varlen(seed: int = 0, n_seqs: int = 8, lo: int = 128, hi: int = 8192
 def retire_plan(rng, live_slots: np.ndarray, P: int):
     """Retire a seeded half of the live rows and compact by hole filling: the
     surviving rows that sit at or above the new live count move down into the
-    free slots below it.  Returns (survivors' new slots, src, dst).
-    Index bookkeeping only; src and dst never overlap."""
+    free slots below it.  Returns (keep mask over live_slots, the survivors'
+    new slots in the same order, src, dst).  Index bookkeeping only; src and
+    dst never overlap and dst entries are distinct."""
     live = np.asarray(live_slots, np.int64)
     n = live.size
     keep_mask = np.zeros(n, bool)
@@ -185,4 +186,4 @@ def retire_plan(rng, live_slots: np.ndarray, P: int):
     assert len(holes) == len(movers)
     remap = dict(zip(movers, holes))
     new_slots = np.array([remap.get(int(s), int(s)) for s in kept], np.int32)
-    return new_slots, np.array(movers, np.int32), np.array(holes, np.int32)
+    return keep_mask, new_slots, np.array(movers, np.int32), np.array(holes, np.int32)
