@@ -1,0 +1,382 @@
+"""Benchmark of the Gated DeltaNet layer core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline (`value`): batched decode at one rank's share of the heads, B = 16
+rows, Hk = 8, Hv = 16, dk = dv = 128, bf16 activations, f32 state, 64-slot
+pool.  One step = gdn_conv_update + gdn_decode_batch for the 16 rows of one
+layer.  Steps rotate over 16 layer replicas (pools, weights and inputs) so
+that every step streams its state from HBM rather than from the 256 MB
+last-level cache, as consecutive layers of a model do.
+
+Also reported on the same JSON line:
+  roofline      the decode kernel: algorithmic bytes per launch / its mean
+                duration from HIP events on the launch stream, against 8 TB/s;
+  prefill       4096-token single-sequence prefill (Hk=8, Hv=16) and the
+                8-sequence packed varlen prefill (Hk=16, Hv=32): tokens/s and
+                algorithmic MFMA fraction;
+  serving       B = 256 rows through 48 layers (Hk=16, Hv=32, 320-slot pools)
+                with a retire + compaction event every 16 steps;
+  cpu_baseline  the f64 oracle on the host cores, on a bounded sample of the
+                headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN decode tokens/s + % HBM peak; chunked prefill tokens/s + % MFMA"
+HBM_PEAK = 8.0e12            # bytes/s
+BF16_PEAK = 2.5e15           # dense MFMA flop/s
+F32_MFMA_PEAK = 157.3e12     # dense f32 MFMA flop/s
+PREFILL_FLOP_PER_TOKEN_HEAD = 180_224   # chunk contractions at d = 128, L = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline decode only (for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+
+
+def _t(x, dtype):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
+
+
+class DecodeLayer:
+    """Device copies of one layer's weights, pool and one step of inputs."""
+
+    def __init__(self, gdn, geom, data, act):
+        import torch
+        self.keep = dict(conv_w=_t(data["weights"]["conv_w"], act),
+                         A_log=_t(data["weights"]["A_log"], torch.float32),
+                         dt_bias=_t(data["weights"]["dt_bias"], torch.float32),
+                         norm_w=_t(data["weights"]["norm_w"], torch.float32))
+        self.w = gdn.LayerWeights(geom, **{"conv_weight": self.keep["conv_w"],
+                                           "A_log": self.keep["A_log"],
+                                           "dt_bias": self.keep["dt_bias"],
+                                           "norm_weight": self.keep["norm_w"]})
+        self.rec = _t(data["rec"], torch.float32)
+        self.conv = _t(data["conv"], act)
+        self.pool = gdn.StatePool(geom, self.rec, self.conv)
+        self.slot = _t(data["slot_idx"], torch.int32)
+        self.x = _t(data["x"], act)
+        self.z = _t(data["z"], act)
+        self.a = _t(data["a"], act)
+        self.b = _t(data["b"], act)
+
+
+def decode_bytes(geom, B, act_bytes):
+    """Algorithmic bytes of one gdn_decode_batch launch: the state tile read
+    and written once, the f32 conv outputs it consumes, z, a, b and y."""
+    C, Hv, dk, dv = geom.channels, geom.num_v_heads, geom.head_k_dim, geom.head_v_dim
+    return B * (8 * Hv * dk * dv + 4 * C + 2 * Hv * dv * act_bytes + 2 * Hv * act_bytes)
+
+
+def step_bytes(geom, B, act_bytes):
+    """Algorithmic bytes of one decode step (conv update + decode) per layer:
+    state read + write, conv window (K-1 columns read, K written), the token's
+    fused input, z, a, b and y."""
+    C, Hv, dk, dv, K = (geom.channels, geom.num_v_heads, geom.head_k_dim, geom.head_v_dim,
+                        geom.conv_kernel)
+    return B * (8 * Hv * dk * dv + (2 * K - 1) * C * act_bytes + C * act_bytes
+                + 2 * Hv * dv * act_bytes + 2 * Hv * act_bytes)
+
+
+# ------------------------------------------------------------------ decode
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import linear_attention_causal_amd as gdn
+    import workloads as wl
+
+    work = wl.decode_batch(seed=0)
+    s = work.shape
+    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                        s.conv_kernel, s.act)
+    act = torch.bfloat16
+    B = len(work.data["slot_idx"])
+    layers = [DecodeLayer(gdn, geom, work.data, act) for _ in range(args.replicas)]
+    qkv = torch.empty(B, geom.channels, device="cuda")
+    y = torch.empty(B, geom.num_v_heads, geom.head_v_dim, device="cuda", dtype=act)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        L = layers[i % len(layers)]
+        gdn.gdn_conv_update(geom, L.w, L.pool, L.slot, L.x, qkv, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        gdn.gdn_decode_batch(geom, L.w, L.pool, L.slot, qkv, L.z, L.a, L.b, y, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    per_launch = decode_bytes(geom, B, 2)
+    achieved = per_launch / (kern_ms * 1e-3)
+    return dict(
+        tokens_per_s=B * args.steps / dt, ms_per_step=dt * 1e3 / args.steps, B=B,
+        workload=work.name, geom=geom,
+        roofline={"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                  "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
+                  "kernel": "gdn::decode_kernel<bf16, 128, 256>",
+                  "bytes_per_launch": per_launch, "mean_launch_us": kern_ms * 1e3},
+        step_hbm_frac=step_bytes(geom, B, 2) / (dt / args.steps) / HBM_PEAK)
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def bench_prefill(work, iters, replicas):
+    import numpy as np
+    import torch
+
+    import linear_attention_causal_amd as gdn
+
+    s, d = work.shape, work.data
+    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                        s.conv_kernel, s.act)
+    act = torch.bfloat16
+    cu = d["cu_seqlens"]
+    T, N = int(cu[-1]), len(cu) - 1
+    w = dict(conv_w=_t(d["weights"]["conv_w"], act), A_log=_t(d["weights"]["A_log"], torch.float32),
+             dt_bias=_t(d["weights"]["dt_bias"], torch.float32),
+             norm_w=_t(d["weights"]["norm_w"], torch.float32))
+    lw = gdn.LayerWeights(geom, w["conv_w"], w["A_log"], w["dt_bias"], w["norm_w"])
+    rec = _t(d["rec"], torch.float32)
+    conv = _t(d["conv"], act)
+    pool = gdn.StatePool(geom, rec, conv)
+    inputs = []
+    x0, z0, a0, b0 = (_t(d[k], act) for k in ("x", "z", "a", "b"))
+    for r in range(replicas):
+        inputs.append((x0.clone(), z0.clone(), a0.clone(), b0.clone()))
+    del x0, z0, a0, b0
+    cu_d = _t(cu, torch.int32)
+    slots = _t(d["slot_idx"], torch.int32)
+    has_init = _t(d["has_init"], torch.uint8)
+    y = torch.empty(T, geom.num_v_heads, geom.head_v_dim, device="cuda", dtype=act)
+    scratch = torch.empty(gdn.gdn_prefill_scratch_bytes(geom, T, N), device="cuda",
+                          dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        x, z, a, b = inputs[i % replicas]
+        gdn.gdn_prefill_chunked(geom, lw, pool, cu, cu_d, slots, x, z, a, b, y, scratch,
+                                has_init=has_init, stream=stream)
+
+    call(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record(stream)
+        call(i + 1)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    flops = PREFILL_FLOP_PER_TOKEN_HEAD * T * geom.num_v_heads * (geom.head_k_dim / 128) ** 2
+    return {"workload": work.name, "tokens": T, "sequences": N, "ms_per_call": ms,
+            "tokens_per_s": T / (ms * 1e-3),
+            "algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac_of_bf16_peak": flops / (ms * 1e-3) / BF16_PEAK,
+            "mfma_frac_of_f32_peak": flops / (ms * 1e-3) / F32_MFMA_PEAK,
+            "mfma_dtype": "f32", "kernels": 3}
+
+
+# ------------------------------------------------------------------ serving
+
+
+def bench_serving(steps=32, layers=48, B=256, P=320):
+    """B rows through `layers` layers per step; after every 16 steps a seeded
+    half of the rows retire, survivors are compacted across all layers and
+    new rows are admitted (zero state).  Pools and inputs are drawn on the
+    device from a seeded generator."""
+    import numpy as np
+    import torch
+
+    import linear_attention_causal_amd as gdn
+    import workloads as wl
+
+    s = wl.FULL_HEADS
+    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                        s.conv_kernel, s.act)
+    act = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    rng = np.random.default_rng(0)
+    C = geom.channels
+    Ls = []
+    for _ in range(layers):
+        w = wl.layer_weights(rng, s)
+        keep = (_t(w["conv_w"], act), _t(w["A_log"], torch.float32),
+                _t(w["dt_bias"], torch.float32), _t(w["norm_w"], torch.float32))
+        rec = torch.randn(P, s.num_v_heads, s.head_k_dim, s.head_v_dim, device="cuda",
+                          generator=gen) * 0.1
+        conv = (torch.randn(P, s.conv_kernel, C, device="cuda", generator=gen) * 0.1).to(act)
+        Ls.append(dict(keep=keep, w=gdn.LayerWeights(geom, *keep), rec=rec, conv=conv,
+                       pool=gdn.StatePool(geom, rec, conv)))
+    live = np.sort(rng.choice(P, B, replace=False)).astype(np.int32)
+    x = (torch.randn(B, C, device="cuda", generator=gen)).to(act)
+    z = torch.randn(B, s.num_v_heads, s.head_v_dim, device="cuda", generator=gen).to(act)
+    a = torch.randn(B, s.num_v_heads, device="cuda", generator=gen).to(act)
+    b = torch.randn(B, s.num_v_heads, device="cuda", generator=gen).to(act)
+    qkv = torch.empty(B, C, device="cuda")
+    y = torch.empty(B, s.num_v_heads, s.head_v_dim, device="cuda", dtype=act)
+    stream = torch.cuda.current_stream()
+    pools = [L["pool"] for L in Ls]
+    compact_ms = []
+
+    def run(nsteps, live):
+        slot_d = _t(live, torch.int32)
+        for t in range(nsteps):
+            if t > 0 and t % 16 == 0:
+                keep, new_slots, src, dst = wl.retire_plan(rng, live, P)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                if src.size:
+                    gdn.gdn_state_compact(geom, pools, src, dst, _t(src, torch.int32),
+                                          _t(dst, torch.int32), stream=stream)
+                e1.record(stream)
+                compact_ms.append((e0, e1, int(src.size)))
+                admitted = np.arange(len(new_slots), len(new_slots) + (len(live) - len(new_slots)),
+                                     dtype=np.int32)
+                live = np.concatenate([new_slots, admitted]).astype(np.int32)
+                slot_d = _t(live, torch.int32)
+            for L in Ls:
+                gdn.gdn_conv_update(geom, L["w"], L["pool"], slot_d, x, qkv, stream=stream)
+                gdn.gdn_decode_batch(geom, L["w"], L["pool"], slot_d, qkv, z, a, b, y,
+                                     stream=stream)
+        return live
+
+    live = run(2, live)
+    torch.cuda.synchronize()
+    compact_ms.clear()
+    t0 = time.perf_counter()
+    run(steps, live)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    cms = [a_.elapsed_time(b_) for a_, b_, _ in compact_ms]
+    moved = [n for _, _, n in compact_ms]
+    per_step = layers * step_bytes(geom, B, 2)
+    return {"workload": f"decode_b{B}_hk16_hv32_d128_p{P}_x{layers}layers",
+            "tokens_per_s": B * steps / dt, "ms_per_step": dt * 1e3 / steps,
+            "hbm_frac_algorithmic": per_step * steps / dt / HBM_PEAK,
+            "compaction_events": len(cms), "compaction_ms": cms, "compaction_pairs": moved,
+            "steps": steps}
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+
+def cpu_baseline(seconds):
+    """The f64 oracle (as it stands) on the host cores: decode steps of the
+    headline workload (16 rows, Hk=8, Hv=16, d=128), repeated until about
+    `seconds` of wall time has passed."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    work = wl.decode_batch(seed=0)
+    s, d = work.shape, work.data
+    og = oracle.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                         s.conv_kernel)
+    ow = oracle.Weights(d["weights"]["conv_w"], d["weights"]["A_log"], d["weights"]["dt_bias"],
+                        d["weights"]["norm_w"])
+    S, W = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
+    B = len(d["slot_idx"])
+    threads = oracle.default_threads()
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        oracle.pool_run(og, ow, S, W, np.arange(B + 1), d["slot_idx"], d["x"], d["z"], d["a"],
+                        d["b"], nthreads=threads)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": B * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode steps of the headline workload (16 rows x 16 V-heads, "
+                      f"d=128) in {dt:.1f} s, f64, one thread per (row, V-head) unit"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import linear_attention_causal_amd as gdn
+
+    gdn.library()
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    log("[bench] decode headline")
+    dec = bench_decode(args)
+    line = {
+        "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": dec["workload"], "rows": dec["B"], "num_k_heads": 8,
+                   "num_v_heads": 16, "head_dim": 128, "conv_kernel": 4, "pool_slots": 64,
+                   "activations": "bf16", "state": "f32",
+                   "cold_cache": f"{args.replicas} rotating layer replicas"},
+        "step_hbm_frac_algorithmic": dec["step_hbm_frac"],
+        "roofline": dec["roofline"],
+    }
+    if not args.no_extras:
+        import workloads as wl
+        log("[bench] prefill t4096")
+        pre = [bench_prefill(wl.prefill_single(seed=0), iters=10, replicas=6)]
+        torch.cuda.empty_cache()
+        log("[bench] prefill varlen8")
+        pre.append(bench_prefill(wl.prefill_varlen(seed=0), iters=5, replicas=1))
+        torch.cuda.empty_cache()
+        line["prefill"] = pre
+        log("[bench] serving 48 layers")
+        line["serving"] = bench_serving()
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
