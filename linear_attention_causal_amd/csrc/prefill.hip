@@ -7,27 +7,28 @@
 // the gates g and beta_i the write strengths (both per V-head),
 //   A   = strict_lower(beta_i e^{gamma_i - gamma_j} k_i . k_j)
 //   Tm  = (I + A)^{-1}                                  (unit lower triangular)
-//   W   = Tm diag(beta e^gamma) K,     U = Tm diag(beta) V
-//   V'  = U - W S                       (the delta-rule writes u_t of the chunk)
-//   O   = diag(e^gamma) Q S + (mask_{j<=i} e^{gamma_i-gamma_j} Q K^T) V'
-//   S  <- e^{gamma_last} S + (diag(e^{gamma_last-gamma}) K)^T V'
+//   V'  = Tm diag(beta) (V - diag(e^gamma) K S)         (the writes u_t)
+//   O   = diag(e^gamma) Q S + P V',   P = mask_{j<=i}(e^{gamma_i-gamma_j}) * (Q K^T)
+//   S  <- e^{gamma_last} S + K^T diag(e^{gamma_last-gamma}) V'
 // which is the token recurrence S_t = e^{g_t}S_{t-1} + beta_t k_t (v_t -
-// e^{g_t} S_{t-1}^T k_t)^T, o_t = S_t^T q_t unrolled over the chunk.  Decays
-// are only ever formed as e^{gamma_i - gamma_j} with j <= i (<= 1), never as a
-// ratio of two underflowing products.
+// e^{g_t} S_{t-1}^T k_t)^T, o_t = S_t^T q_t unrolled over the chunk (the
+// usual WY/UT form with W = Tm diag(beta e^gamma) K never formed: Tm is
+// applied to the small chunk x dv right-hand side instead).  Decays are only
+// formed as e^{gamma_i - gamma_j} with j <= i (<= 1).
 //
-// Three launches, in stream order:
-//   1. prep   (chunk, sequence, K-head), all chunks in parallel: conv + SiLU,
-//             l2norm, gates and their in-chunk running sum, the Gram matrix
-//             K K^T shared by the V-heads of the K-head, the triangular
-//             solve, W and U.
+// Launches, in stream order:
+//   0. plan   one workgroup: chunk_base[n] = number of chunks before sequence n.
+//   1. prep   (chunk, sequence, K-head), all chunks in parallel: conv + SiLU
+//             of q/k, l2norm, K K^T and Q K^T once per K-head; per V-head the
+//             gates, their running sum, Tm (blocked 16 x 16 triangular
+//             inverse) and P.  Operands are written as bf16 (hi, lo) pairs in
+//             the exact fragment layout of the next kernel.
 //   2. state  (sequence, V-head, dv tile), sequential over the chunks of a
-//             sequence: V' = U - W S, the inter-chunk part of O, and the state
-//             carry.  dv columns of S evolve independently, so tiles of
-//             columns run in parallel.  Also writes the final conv window.
-//   3. output (chunk, sequence, V-head), in parallel: intra-chunk attention
-//             P V', gated RMSNorm with SiLU(z).
-// Products run on MFMA (v_mfma_f32_16x16x4_f32) from LDS-staged f32 tiles.
+//             sequence, the dv columns of S split over workgroups (they
+//             evolve independently): K S, Q S, V', P V' and the state carry,
+//             on 3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo + lo*hi with f32
+//             accumulation, about 2^-16 relative), then O (pre-norm) to f32.
+//   3. norm   (chunk, sequence, V-head): gated RMSNorm with SiLU(z) -> y.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -37,39 +38,72 @@ constexpr int kL = 64;        // chunk length
 constexpr int kNT = 256;      // threads per workgroup (4 waves)
 constexpr int kNW = kNT / 64;
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Token-indexed scratch: every array is addressed by the packed token index,
-// so no per-sequence offsets are needed.
+// Chunk-indexed scratch: chunk g = chunk_base[n] + c holds 64 rows (rows past
+// the end of a sequence are written as zeros by the prep kernel).
 struct PrefillScratch {
-  float* qh;   // [T][Hk][D]  q_hat (l2-normalised, scaled)
-  float* kh;   // [T][Hk][D]  k_hat
-  float* w;    // [T][Hv][D]  W rows
-  float* u;    // [T][Hv][D]  U rows, overwritten by V' in the state pass
-  float* oi;   // [T][Hv][D]  e^gamma Q S (inter-chunk part of O)
-  float* gam;  // [T][Hv]     in-chunk running sum of g
+  int32_t* chunk_base;     // [N+1]
+  __bf16* qh[2];           // hi, lo: [G][Hk][64][D]   q_hat rows
+  __bf16* kh[2];           //         [G][Hk][64][D]   k_hat rows
+  __bf16* kt[2];           //         [G][Hk][D][64]   k_hat transposed
+  __bf16* tm[2];           //         [G][Hv][64][64]  (I + A)^{-1}
+  __bf16* pm[2];           //         [G][Hv][64][64]  masked, decayed Q K^T
+  float* gam;              // [G][Hv][64] running sum of g
+  float* beta;             // [G][Hv][64]
+  float* o;                // [T][Hv][D] pre-norm output
 };
 
-size_t prefill_scratch_bytes(const gdn_geometry& g, long long T, long long /*N*/) {
-  const size_t D = (size_t)g.head_k_dim;
-  const size_t qk = align256((size_t)T * g.num_k_heads * D * 4);
-  const size_t hv = align256((size_t)T * g.num_v_heads * D * 4);
-  const size_t gm = align256((size_t)T * g.num_v_heads * 4);
-  return 2 * qk + 3 * hv + gm;
+static size_t chunk_bound(long long T, long long N) { return (size_t)((T + kL - 1) / kL + N); }
+
+struct ScratchPlan {
+  size_t off[14];
+  size_t total;
+};
+
+static ScratchPlan plan_scratch(const gdn_geometry& g, long long T, long long N) {
+  const size_t G = chunk_bound(T, N), D = (size_t)g.head_k_dim;
+  const size_t Hk = (size_t)g.num_k_heads, Hv = (size_t)g.num_v_heads;
+  const size_t sizes[14] = {
+      (size_t)(N + 1) * 4,
+      G * Hk * kL * D * 2, G * Hk * kL * D * 2,      // qh
+      G * Hk * kL * D * 2, G * Hk * kL * D * 2,      // kh
+      G * Hk * D * kL * 2, G * Hk * D * kL * 2,      // kt
+      G * Hv * kL * kL * 2, G * Hv * kL * kL * 2,    // tm
+      G * Hv * kL * kL * 2, G * Hv * kL * kL * 2,    // pm
+      G * Hv * kL * 4, G * Hv * kL * 4,              // gam, beta
+      (size_t)T * Hv * D * 4};                       // o
+  ScratchPlan sp;
+  size_t at = 0;
+  for (int i = 0; i < 14; ++i) {
+    sp.off[i] = at;
+    at += align256(sizes[i]);
+  }
+  sp.total = at;
+  return sp;
 }
 
-static PrefillScratch carve(const gdn_geometry& g, long long T, void* base) {
-  const size_t D = (size_t)g.head_k_dim;
-  const size_t qk = align256((size_t)T * g.num_k_heads * D * 4);
-  const size_t hv = align256((size_t)T * g.num_v_heads * D * 4);
+size_t prefill_scratch_bytes(const gdn_geometry& g, long long T, long long N) {
+  return plan_scratch(g, T, N).total;
+}
+
+static PrefillScratch carve(const gdn_geometry& g, long long T, long long N, void* base) {
+  const ScratchPlan sp = plan_scratch(g, T, N);
   char* c = static_cast<char*>(base);
   PrefillScratch s;
-  s.qh = reinterpret_cast<float*>(c); c += qk;
-  s.kh = reinterpret_cast<float*>(c); c += qk;
-  s.w = reinterpret_cast<float*>(c); c += hv;
-  s.u = reinterpret_cast<float*>(c); c += hv;
-  s.oi = reinterpret_cast<float*>(c); c += hv;
-  s.gam = reinterpret_cast<float*>(c);
+  s.chunk_base = reinterpret_cast<int32_t*>(c + sp.off[0]);
+  for (int k = 0; k < 2; ++k) {
+    s.qh[k] = reinterpret_cast<__bf16*>(c + sp.off[1 + k]);
+    s.kh[k] = reinterpret_cast<__bf16*>(c + sp.off[3 + k]);
+    s.kt[k] = reinterpret_cast<__bf16*>(c + sp.off[5 + k]);
+    s.tm[k] = reinterpret_cast<__bf16*>(c + sp.off[7 + k]);
+    s.pm[k] = reinterpret_cast<__bf16*>(c + sp.off[9 + k]);
+  }
+  s.gam = reinterpret_cast<float*>(c + sp.off[11]);
+  s.beta = reinterpret_cast<float*>(c + sp.off[12]);
+  s.o = reinterpret_cast<float*>(c + sp.off[13]);
   return s;
 }
 
@@ -79,7 +113,7 @@ struct PrefillParams {
   const void* a;        // [T][Hv] act
   const void* b;        // [T][Hv] act
   void* y;              // [T][Hv][D] act
-  float* o_raw;         // [T][Hv][D] f32 or null
+  float* obuf;          // [T][Hv][D] f32: caller's o_raw or scratch
   float* rec;           // [P][Hv][D][D]
   void* conv;           // [P][K][C] act
   const int32_t* cu;    // [N+1]
@@ -116,19 +150,28 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int n) {
 
 // Raw (pre-conv) input of channel ch at position rel relative to the start of
 // the sequence; negative positions come from the slot's conv window (whose
-// last column is position -1) or are zero for a fresh sequence.
+// last column is position -1) or are zero for a fresh sequence; `valid`
+// false gives zero.  Branch-free: the address is always a readable element
+// (the load is unconditional and the value is selected afterwards), so that
+// a conditional load never forces a wait on every outstanding load.
 template <typename Act, int K>
 __device__ __forceinline__ float raw_input(const PrefillParams& p, const SeqInfo& si,
-                                           long long rel, int ch) {
+                                           long long rel, int ch, bool valid = true) {
   using io = act_io<Act>;
-  if (rel >= 0) return io::load(p.x, (size_t)(si.begin + rel) * p.C + ch);
-  if (!si.init) return 0.f;
+  const bool in_x = rel >= 0;
+  const bool use = valid && (in_x ? rel < si.len : (si.init && rel >= -K));
   const void* win = static_cast<const char*>(p.conv) + (size_t)si.slot * K * p.C * io::bytes;
-  return io::load(win, (size_t)(K + rel) * p.C + ch);
+  const void* base = (use && in_x) ? p.x : win;
+  const size_t idx = !use ? (size_t)ch
+                   : in_x ? (size_t)(si.begin + rel) * p.C + ch
+                          : (size_t)(K + rel) * p.C + ch;
+  const float v = io::load(base, idx);
+  return use ? v : 0.f;
 }
 
 // Causal conv + SiLU of one channel over tokens t0 .. t0+nc-1 of a sequence;
-// out[i * ld] for i < kL (rows >= nc get zero).
+// out[i * ld] for i < kL (rows >= nc get zero).  All kL + K - 1 inputs are
+// requested before any arithmetic so that their latencies overlap.
 template <typename Act, int K>
 __device__ __forceinline__ void conv_channel(const PrefillParams& p, const SeqInfo& si,
                                              int t0, int nc, int ch, float* out, int ld) {
@@ -136,60 +179,183 @@ __device__ __forceinline__ void conv_channel(const PrefillParams& p, const SeqIn
   float wt[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) wt[j] = io::load(p.conv_w, (size_t)ch * K + j);
-  float hist[K - 1];  // positions t0-(K-1) .. t0-1
+  float xs[kL + K - 1];  // positions t0-(K-1) .. t0+kL-1
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) hist[j] = raw_input<Act, K>(p, si, (long long)t0 - (K - 1) + j, ch);
+  for (int j = 0; j < K - 1; ++j) xs[j] = raw_input<Act, K>(p, si, (long long)t0 - (K - 1) + j, ch);
+  const size_t base = (size_t)(si.begin + t0) * p.C + ch;
+#pragma unroll
+  for (int i = 0; i < kL; ++i) {  // clamped address, then select: no branch per load
+    const float v = io::load(p.x, base + (size_t)min(i, nc - 1) * p.C);
+    xs[K - 1 + i] = i < nc ? v : 0.f;
+  }
+#pragma unroll
   for (int i = 0; i < kL; ++i) {
-    float v = 0.f;
-    if (i < nc) {
-      const float xc = io::load(p.x, (size_t)(si.begin + t0 + i) * p.C + ch);
-      float acc = wt[K - 1] * xc;
+    float acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < K - 1; ++j) acc = fmaf(wt[j], hist[j], acc);
-#pragma unroll
-      for (int j = 0; j < K - 2; ++j) hist[j] = hist[j + 1];
-      hist[K - 2] = xc;
-      v = silu(acc);
-    }
-    out[i * ld] = v;
+    for (int j = 0; j < K; ++j) acc = fmaf(wt[j], xs[i + j], acc);
+    out[i * ld] = i < nc ? silu(acc) : 0.f;
   }
 }
+
+// --------------------------------------------------------------- MFMA helpers
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Tm = (I + A)^{-1} for strictly lower-triangular A [kL][kL + 4] in LDS, by
-// one wave: lane j solves column j by forward substitution, holding it in
-// registers; rows of A are read as broadcasts.  Kept out of line so that it
-// is compiled once for all kernel instantiations.
-__device__ __attribute__((noinline)) void unit_lower_inverse(const float* sA, float* sT,
-                                                            int lane) {
-  constexpr int LDL = kL + 4;
-  float tcol[kL];
+// Lane layout of v_mfma_f32_16x16x32_bf16: A[i][k] at lane i + 16*(k/8),
+// element k%8; B[k][j] at lane j + 16*(k/8), element k%8; D[i][j] at lane
+// j + 16*(i/4), element i%4.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// c += (ah + al)(bh + bl), dropping the al*bl term (small terms first).
+__device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+  c = mfma_bf16(al, bh, c);
+  c = mfma_bf16(ah, bl, c);
+  return mfma_bf16(ah, bh, c);
+}
+
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(v);
+  lo = static_cast<__bf16>(v - static_cast<float>(hi));
+}
+
+// Eight consecutive f32 from LDS split into bf16 (hi, lo) fragments.
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
-  for (int i = 0; i < kL; ++i) {
-    float acc = i == lane ? 1.f : 0.f;
-#pragma unroll
-    for (int j = 0; j < i; ++j) acc = fmaf(-sA[i * LDL + j], tcol[j], acc);
-    tcol[i] = acc;
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h, l;
+    split_bf16(v[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
   }
+}
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// ------------------------------------------------------------------ 0. plan
+
+// chunk_base[n] = sum over n' < n of ceil(len(n') / 64), chunk_base[N] = total.
+// One workgroup of 1024 threads: per-thread partial sums over a contiguous
+// range of sequences, then a wave64 shuffle scan and a scan of wave totals.
+__device__ __forceinline__ int seq_chunks(const int32_t* cu, int n, long long T) {
+  long long b = cu[n], e = cu[n + 1];
+  if (b < 0 || e > T || e < b) return 0;
+  return (int)((e - b + kL - 1) / kL);
+}
+
+__global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t* cu, int N, long long T,
+                                                            int32_t* chunk_base) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (N + 1023) / 1024;
+  const int n0 = tid * per, n1 = min(N, n0 + per);
+  int local = 0;
+  for (int n = n0; n < n1; ++n) local += seq_chunks(cu, n, T);
+  int incl = local;
 #pragma unroll
-  for (int i = 0; i < kL; ++i) sT[i * LDL + lane] = tcol[i];
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int v = wsum[w];
+      wsum[w] = run;
+      run += v;
+    }
+    chunk_base[N] = run;
+  }
+  __syncthreads();
+  int run = wsum[wave] + incl - local;
+  for (int n = n0; n < n1; ++n) {
+    chunk_base[n] = run;
+    run += seq_chunks(cu, n, T);
+  }
 }
 
 // ------------------------------------------------------------------ 1. prep
 
+// C[16x16] += A[16x16] B[16x16] on f32 MFMA, operands in LDS.
+__device__ __forceinline__ f32x4 mm16(const float* A, int lda, const float* B, int ldb,
+                                      f32x4 acc, int lane) {
+  const int li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    acc = mfma_f32(A[li * lda + 4 * ks + lk], B[(4 * ks + lk) * ldb + li], acc);
+  return acc;
+}
+
+// Tm = (I + A)^{-1} for strictly lower-triangular A [64][LDL] in LDS, blocked
+// by 16: the four diagonal blocks by forward substitution (one lane per
+// column), then T_ij = -T_ii sum_{j<=k<i} A_ik T_kj by distance i - j.
+// Called by all four waves; ends with the result in sT.
+template <int LDL>
+__device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  // strictly upper blocks are zero
+  for (int idx = tid; idx < kL * kL; idx += kNT) {
+    const int i = idx / kL, j = idx - i * kL;
+    if ((j >> 4) > (i >> 4)) sT[i * LDL + j] = 0.f;
+  }
+  if (lane < 16) {
+    const int b0 = 16 * wave, c = lane;
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = i == c ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) acc = fmaf(-sA[(b0 + i) * LDL + b0 + j], t[j], acc);
+      t[i] = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(b0 + i) * LDL + b0 + c] = t[i];
+  }
+  __syncthreads();
+  float* M = sM + wave * 16 * 17;
+#pragma unroll
+  for (int dist = 1; dist < 4; ++dist) {
+    const int jb = wave, ib = wave + dist;
+    const bool act = ib < 4;
+    if (act) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = jb; kb < ib; ++kb)
+        acc = mm16(sA + 16 * ib * LDL + 16 * kb, LDL, sT + 16 * kb * LDL + 16 * jb, LDL, acc, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) M[(4 * lk + e) * 17 + li] = acc[e];
+    }
+    __syncthreads();
+    if (act) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm16(sT + 16 * ib * LDL + 16 * ib, LDL, M, 17, acc, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[(16 * ib + 4 * lk + e) * LDL + 16 * jb + li] = -acc[e];
+    }
+    __syncthreads();
+  }
+}
+
 template <typename Act, int D, int K>
 __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   using io = act_io<Act>;
-  constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16;
-  __shared__ float sK[kL * LDD];
-  __shared__ float sV[kL * LDD];
-  __shared__ float sG[kL * LDL];
-  __shared__ float sA[kL * LDL];
-  __shared__ float sT[kL * LDL];
-  __shared__ float sGam[kL], sBeta[kL], sCoef[kL];
+  constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NKS = D / 32;
+  constexpr int TILE = kL * (LDD > LDL ? LDD : LDL);
+  __shared__ __attribute__((aligned(16))) float sQ[TILE];   // q_hat; later A
+  __shared__ __attribute__((aligned(16))) float sK[TILE];   // k_hat; later Tm
+  __shared__ float sG[kL * LDL];                                // K K^T
+  __shared__ float sQK[kL * LDL];                               // Q K^T
+  __shared__ float sM[kNW * 16 * 17];
+  __shared__ float sGam[kL], sBeta[kL];
+  float* sA = sQ;
+  float* sT = sK;
 
   const int c = blockIdx.x, n = blockIdx.y, m = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
@@ -197,100 +363,126 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   if (si.slot < 0 || t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
   const long long tok0 = si.begin + t0;
+  const size_t g = (size_t)p.s.chunk_base[n] + c;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
 
-  // conv + SiLU of q_m (into sV for now) and k_m (into sK)
+  // conv + SiLU of q_m and k_m
   for (int e = tid; e < 2 * D; e += kNT) {
     if (e < D)
-      conv_channel<Act, K>(p, si, t0, nc, m * D + e, sV + e, LDD);
+      conv_channel<Act, K>(p, si, t0, nc, m * D + e, sQ + e, LDD);
     else
       conv_channel<Act, K>(p, si, t0, nc, (p.Hk + m) * D + (e - D), sK + (e - D), LDD);
   }
   __syncthreads();
-
-  // l2norm of each token's q and k; q_hat, k_hat to scratch, k_hat kept in LDS
+  // l2norm (q also scaled)
   for (int i = wave; i < nc; i += kNW) {
     float sq = 0.f, sk = 0.f;
     for (int d = lane; d < D; d += 64) {
-      const float qv = sV[i * LDD + d], kv = sK[i * LDD + d];
+      const float qv = sQ[i * LDD + d], kv = sK[i * LDD + d];
       sq = fmaf(qv, qv, sq);
       sk = fmaf(kv, kv, sk);
     }
     sq = wave_sum(sq);
     sk = wave_sum(sk);
     const float rq = p.scale / sqrtf(sq + p.l2eps), rk = 1.0f / sqrtf(sk + p.l2eps);
-    const size_t o = ((size_t)(tok0 + i) * p.Hk + m) * D;
     for (int d = lane; d < D; d += 64) {
-      const float kv = sK[i * LDD + d] * rk;
-      sK[i * LDD + d] = kv;
-      p.s.kh[o + d] = kv;
-      p.s.qh[o + d] = sV[i * LDD + d] * rq;
+      sQ[i * LDD + d] *= rq;
+      sK[i * LDD + d] *= rk;
     }
   }
   __syncthreads();
-
-  // Gram matrix G = K K^T, lower block triangle only
-  for (int t = wave; t < NTL * (NTL + 1) / 2; t += kNW) {
-    int I = 0, rem = t;
+  // q_hat, k_hat rows and k_hat^T as bf16 (hi, lo) fragments
+  {
+    const size_t rows = (g * p.Hk + m) * kL;
+    for (int u = tid; u < kL * (D / 8); u += kNT) {
+      const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
+      bf16x8 h, l;
+      split8(sQ + i * LDD + d0, h, l);
+      *reinterpret_cast<bf16x8*>(p.s.qh[0] + (rows + i) * D + d0) = h;
+      *reinterpret_cast<bf16x8*>(p.s.qh[1] + (rows + i) * D + d0) = l;
+      split8(sK + i * LDD + d0, h, l);
+      *reinterpret_cast<bf16x8*>(p.s.kh[0] + (rows + i) * D + d0) = h;
+      *reinterpret_cast<bf16x8*>(p.s.kh[1] + (rows + i) * D + d0) = l;
+    }
+    const size_t trow = (g * p.Hk + m) * D;
+    for (int u = tid; u < D * (kL / 8); u += kNT) {
+      const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d];
+      bf16x8 h, l;
+      split8(v, h, l);
+      *reinterpret_cast<bf16x8*>(p.s.kt[0] + (trow + d) * kL + i0) = h;
+      *reinterpret_cast<bf16x8*>(p.s.kt[1] + (trow + d) * kL + i0) = l;
+    }
+  }
+  // K K^T and Q K^T, lower block triangle, 3-pass bf16
+  for (int t = wave; t < 2 * NTL * (NTL + 1) / 2; t += kNW) {
+    const bool isG = t < NTL * (NTL + 1) / 2;
+    int I = 0, rem = isG ? t : t - NTL * (NTL + 1) / 2;
     while (rem > I) { rem -= I + 1; ++I; }
     const int J = rem;
+    const float* Asrc = isG ? sK : sQ;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < D; k0 += 4)
-      acc = mfma_f32(sK[(16 * I + li) * LDD + k0 + lk], sK[(16 * J + li) * LDD + k0 + lk], acc);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sG[(16 * I + 4 * lk + e) * LDL + 16 * J + li] = acc[e];
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 ah, al, bh, bl;
+      split8(Asrc + (16 * I + li) * LDD + 32 * ks + 8 * lk, ah, al);
+      split8(sK + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
+      acc = mfma3(ah, al, bh, bl, acc);
+    }
+    float* dst = isG ? sG : sQK;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(16 * I + 4 * lk + e) * LDL + 16 * J + li] = acc[e];
   }
-  __syncthreads();
+  __syncthreads();  // q/k tiles are free from here on (reused as A and Tm)
 
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = m * p.r + hh;
-    // conv + SiLU of v_h
-    for (int e = tid; e < D; e += kNT)
-      conv_channel<Act, K>(p, si, t0, nc, 2 * p.Hk * D + h * D + e, sV + e, LDD);
-    // gates and their running sum over the chunk (padding rows: g = beta = 0)
+    const size_t gh = g * p.Hv + h;
     if (wave == 0) {
-      float g = 0.f, beta = 0.f;
+      float gv = 0.f, bv = 0.f;
       if (lane < nc)
         gates(p.A_log[h], p.dt_bias[h], io::load(p.a, (size_t)(tok0 + lane) * p.Hv + h),
-              io::load(p.b, (size_t)(tok0 + lane) * p.Hv + h), g, beta);
+              io::load(p.b, (size_t)(tok0 + lane) * p.Hv + h), gv, bv);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off, 64);
-        if (lane >= off) g += y;
+        const float y = __shfl_up(gv, off, 64);
+        if (lane >= off) gv += y;
       }
-      sGam[lane] = g;
-      sBeta[lane] = beta;
-      sCoef[lane] = beta * expf(g);
-      if (lane < nc) p.s.gam[(size_t)(tok0 + lane) * p.Hv + h] = g;
+      sGam[lane] = gv;
+      sBeta[lane] = bv;
+      p.s.gam[gh * kL + lane] = gv;
+      p.s.beta[gh * kL + lane] = bv;
     }
     __syncthreads();
+    // A (for the inverse) and P (written out as fragments)
     for (int idx = tid; idx < kL * kL; idx += kNT) {
       const int i = idx / kL, j = idx - i * kL;
       sA[i * LDL + j] = j < i ? sBeta[i] * expf(sGam[i] - sGam[j]) * sG[i * LDL + j] : 0.f;
     }
-    __syncthreads();
-    if (wave == 0) unit_lower_inverse(sA, sT, lane);
-    __syncthreads();
-    // W = Tm diag(beta e^gamma) K,  U = Tm diag(beta) V
-    constexpr int NCT = D / 16;
-    for (int t = wave; t < 2 * NTL * NCT; t += kNW) {
-      const bool isW = t < NTL * NCT;
-      const int tt = isW ? t : t - NTL * NCT;
-      const int I = tt / NCT, J = tt - I * NCT;
-      const float* src = isW ? sK : sV;
-      const float* coef = isW ? sCoef : sBeta;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < kL; k0 += 4) {
-        const int kk = k0 + lk;
-        acc = mfma_f32(sT[(16 * I + li) * LDL + kk], src[kk * LDD + 16 * J + li] * coef[kk], acc);
-      }
-      float* dst = isW ? p.s.w : p.s.u;
+    for (int u = tid; u < kL * (kL / 8); u += kNT) {
+      const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+      float v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * I + 4 * lk + e;
-        if (row < nc) dst[((size_t)(tok0 + row) * p.Hv + h) * D + 16 * J + li] = acc[e];
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        v[e] = j <= i ? expf(sGam[i] - sGam[j]) * sQK[i * LDL + j] : 0.f;
       }
+      bf16x8 h8, l8;
+      split8(v, h8, l8);
+      *reinterpret_cast<bf16x8*>(p.s.pm[0] + (gh * kL + i) * kL + j0) = h8;
+      *reinterpret_cast<bf16x8*>(p.s.pm[1] + (gh * kL + i) * kL + j0) = l8;
+    }
+    __syncthreads();
+    unit_lower_inverse<LDL>(sA, sT, sM, tid);
+    for (int u = tid; u < kL * (kL / 8); u += kNT) {
+      const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+      bf16x8 h8, l8;
+      split8(sT + i * LDL + j0, h8, l8);
+      *reinterpret_cast<bf16x8*>(p.s.tm[0] + (gh * kL + i) * kL + j0) = h8;
+      *reinterpret_cast<bf16x8*>(p.s.tm[1] + (gh * kL + i) * kL + j0) = l8;
     }
     __syncthreads();
   }
@@ -298,16 +490,41 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------------ 2. state
 
+constexpr int kSW = 8;             // waves of the state kernel
+constexpr int kSNT = 64 * kSW;
+
+// x * sigmoid(x) with the hardware exp and reciprocal (a few ulp).
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// Operands of one chunk held in registers by one wave: the A fragments of
+// its token-row block (k_hat, q_hat, Tm, P) and of its two state blocks
+// (k_hat^T), plus the raw v inputs of its four token rows.
+template <int NKS, int SPW, int K>
+struct ChunkOps {
+  bf16x8 kq[NKS][4];     // k_hat hi, lo, q_hat hi, lo
+  bf16x8 tp[2][4];       // Tm hi, lo, P hi, lo
+  bf16x8 kt[SPW][2][2];  // [state block][k-step][hi, lo] of k_hat^T
+  float vraw[K + 3];
+  float gam, beta;     // lane < 64: this chunk's row `lane`
+  float glast;
+};
+
 template <typename Act, int D, int DVT, int K>
-__global__ __launch_bounds__(kNT) void prefill_state_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   using io = act_io<Act>;
-  constexpr int LDD = D + 4, LDV = DVT + 4, NCT = DVT / 16;
-  __shared__ float sS[D * LDV];
-  __shared__ float sW[kL * LDD];
-  __shared__ float sQ[kL * LDD];
-  __shared__ float sK[kL * LDD];
-  __shared__ float sVp[kL * LDV];
-  __shared__ float sEg[kL], sDec[kL];
+  constexpr int NCB = DVT / 16;        // 16-wide column blocks of the tile
+  constexpr int NKS = D / 32;          // k-steps over dk
+  constexpr int NST = (D / 16) * NCB;  // 16 x 16 blocks of the state tile
+  constexpr int SPW = (NST + kSW - 1) / kSW;  // ... per wave (at most)
+  constexpr int LS = D + 8;            // row length of the transposed state [j][d]
+  constexpr int LR = kL + 8;           // row length of [j][token] tiles
+  static_assert(NCB * (kL / 16) == kSW, "one 16 x 16 output block per wave");
+  __shared__ __attribute__((aligned(16))) __bf16 sS[2][DVT * LS];   // state, B operand
+  __shared__ __attribute__((aligned(16))) __bf16 sR[2][DVT * LR];   // R, later e^{..} V'
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][DVT * LR];   // V'
+  __shared__ float sEg[kL], sBeta[kL], sDec[kL];
 
   const int n = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * DVT;
   const SeqInfo si = seq_info(p, n);
@@ -315,97 +532,228 @@ __global__ __launch_bounds__(kNT) void prefill_state_kernel(PrefillParams p) {
   const int m = h / p.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
+  const int orb = wave & 3, ocb = wave >> 2;   // this wave's output block
+  const int i0 = 16 * orb + 4 * lk;            // first of this lane's four token rows
+  const int vch = 2 * p.Hk * D + h * D + col0 + 16 * ocb + li;  // its v channel
   float* Sg = p.rec + ((size_t)si.slot * p.Hv + h) * D * D;
+  const size_t cbase = si.len > 0 ? (size_t)p.s.chunk_base[n] : 0;
+  const int nchunks = (si.len + kL - 1) / kL;
 
-  for (int idx = tid; idx < D * DVT; idx += kNT) {
-    const int d = idx / DVT, e = idx - d * DVT;
-    sS[d * LDV + e] = si.init ? Sg[(size_t)d * D + col0 + e] : 0.f;
+  float wt[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) wt[k] = io::load(p.conv_w, (size_t)vch * K + k);
+
+  // state blocks owned by this wave, in accumulator layout
+  // (a wave owns state block st = wave + 8q when st < NST; uniform per wave)
+  auto owns = [&](int q) { return NST % kSW == 0 || wave + kSW * q < NST; };
+  f32x4 S[SPW];
+#pragma unroll
+  for (int q = 0; q < SPW; ++q) {
+    S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!owns(q)) continue;
+    const int st = wave + kSW * q, rb = st / NCB, cb = st - rb * NCB;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li];
+      S[q][e] = si.init ? v : 0.f;
+    }
   }
 
-  const int nchunks = (si.len + kL - 1) / kL;
+  // Loads are unconditional (the chunk index is clamped), so that the
+  // prefetch of chunk c+1 never introduces a branch and its wait.
+  auto load_kq = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+    const size_t gk = (cbase + c) * p.Hk + m;
+    const size_t ro = (gk * kL + 16 * orb + li) * D + 8 * lk;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      o.kq[ks][0] = ld8(p.s.kh[0] + ro + 32 * ks);
+      o.kq[ks][1] = ld8(p.s.kh[1] + ro + 32 * ks);
+      o.kq[ks][2] = ld8(p.s.qh[0] + ro + 32 * ks);
+      o.kq[ks][3] = ld8(p.s.qh[1] + ro + 32 * ks);
+    }
+  };
+  auto load_tp = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+    const size_t gh = (cbase + c) * p.Hv + h;
+    const size_t ro = (gh * kL + 16 * orb + li) * kL + 8 * lk;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      o.tp[ks][0] = ld8(p.s.tm[0] + ro + 32 * ks);
+      o.tp[ks][1] = ld8(p.s.tm[1] + ro + 32 * ks);
+      o.tp[ks][2] = ld8(p.s.pm[0] + ro + 32 * ks);
+      o.tp[ks][3] = ld8(p.s.pm[1] + ro + 32 * ks);
+    }
+  };
+  auto load_kt = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+    const size_t gk = (cbase + c) * p.Hk + m;
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+      const int rb = owns(q) ? (wave + kSW * q) / NCB : 0;
+      const size_t ro = (gk * D + 16 * rb + li) * kL + 8 * lk;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        o.kt[q][ks][0] = ld8(p.s.kt[0] + ro + 32 * ks);
+        o.kt[q][ks][1] = ld8(p.s.kt[1] + ro + 32 * ks);
+      }
+    }
+  };
+  auto load_misc = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+    const int t0 = c * kL, nc = min(kL, si.len - t0);
+    const size_t gh = (cbase + c) * p.Hv + h;
+    o.glast = p.s.gam[gh * kL + nc - 1];
+    o.gam = p.s.gam[gh * kL + lane];
+    o.beta = p.s.beta[gh * kL + lane];
+#pragma unroll
+    for (int k = 0; k < K + 3; ++k) {
+      const int pos = t0 + i0 - (K - 1) + k;  // relative to the sequence start
+      o.vraw[k] = raw_input<Act, K>(p, si, pos, vch, pos < t0 + nc);
+    }
+  };
+
+  ChunkOps<NKS, SPW, K> ops;
+  if (nchunks > 0) {
+    load_kq(ops, 0);
+    load_tp(ops, 0);
+    load_kt(ops, 0);
+    load_misc(ops, 0);
+  }
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kL, nc = min(kL, si.len - t0);
     const long long tok0 = si.begin + t0;
-    __syncthreads();  // previous chunk finished with the LDS tiles
-    const float glast = p.s.gam[(size_t)(tok0 + nc - 1) * p.Hv + h];
-    for (int idx = tid; idx < kL * D; idx += kNT) {
-      const int i = idx / D, d = idx - i * D;
-      float wv = 0.f, qv = 0.f, kv = 0.f;
-      if (i < nc) {
-        wv = p.s.w[((size_t)(tok0 + i) * p.Hv + h) * D + d];
-        const size_t o = ((size_t)(tok0 + i) * p.Hk + m) * D + d;
-        qv = p.s.qh[o];
-        kv = p.s.kh[o];
-      }
-      sW[i * LDD + d] = wv;
-      sQ[i * LDD + d] = qv;
-      sK[i * LDD + d] = kv;
-    }
-    for (int idx = tid; idx < kL * DVT; idx += kNT) {
-      const int i = idx / DVT, e = idx - i * DVT;
-      sVp[i * LDV + e] = i < nc ? p.s.u[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + e] : 0.f;
-    }
+    const int cn = min(c + 1, nchunks - 1);  // chunk whose operands are prefetched
+    __syncthreads();  // the previous chunk is done with every LDS tile
     if (tid < kL) {
-      const float gi = tid < nc ? p.s.gam[(size_t)(tok0 + tid) * p.Hv + h] : glast;
-      sEg[tid] = expf(gi);
-      sDec[tid] = expf(glast - gi);
+      const bool ok = tid < nc;
+      sEg[tid] = ok ? __expf(ops.gam) : 0.f;
+      sBeta[tid] = ok ? ops.beta : 0.f;
+      sDec[tid] = ok ? __expf(ops.glast - ops.gam) : 0.f;
     }
-    __syncthreads();
-
-    // V' = U - W S  and  O_inter = diag(e^gamma) Q S
-    for (int t = wave; t < (kL / 16) * NCT; t += kNW) {
-      const int I = t / NCT, J = t - I * NCT;
-      f32x4 ws = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < D; k0 += 4) {
-        const float bS = sS[(k0 + lk) * LDV + 16 * J + li];
-        ws = mfma_f32(sW[(16 * I + li) * LDD + k0 + lk], bS, ws);
-        qs = mfma_f32(sQ[(16 * I + li) * LDD + k0 + lk], bS, qs);
-      }
+    const float egl = __expf(ops.glast);
+    float v4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc = fmaf(wt[k], ops.vraw[e + k], acc);
+      v4[e] = i0 + e < nc ? silu_fast(acc) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+      if (!owns(q)) continue;
+      const int st = wave + kSW * q, rb = st / NCB, cb = st - rb * NCB;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 16 * I + 4 * lk + e, col = 16 * J + li;
-        const float vp = sVp[row * LDV + col] - ws[e];
-        sVp[row * LDV + col] = vp;
-        if (row < nc) {
-          const size_t o = ((size_t)(tok0 + row) * p.Hv + h) * D + col0 + col;
-          p.s.u[o] = vp;
-          p.s.oi[o] = sEg[row] * qs[e];
-        }
+        __bf16 hi, lo;
+        split_bf16(S[q][e], hi, lo);
+        const int idx = (16 * cb + li) * LS + 16 * rb + 4 * lk + e;
+        sS[0][idx] = hi;
+        sS[1][idx] = lo;
       }
     }
     __syncthreads();
 
-    // S <- e^{gamma_last} S + (diag(e^{gamma_last - gamma}) K)^T V'
-    const float egl = expf(glast);
-    for (int t = wave; t < (D / 16) * NCT; t += kNW) {
-      const int I = t / NCT, J = t - I * NCT;
-      f32x4 acc;
+    // X = K S and Y = Q S for this wave's output block
+    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = egl * sS[(16 * I + 4 * lk + e) * LDV + 16 * J + li];
-      for (int k0 = 0; k0 < kL; k0 += 4) {
-        const int kk = k0 + lk;
-        acc = mfma_f32(sK[kk * LDD + 16 * I + li] * sDec[kk], sVp[kk * LDV + 16 * J + li], acc);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sS[(16 * I + 4 * lk + e) * LDV + 16 * J + li] = acc[e];
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int bo = (16 * ocb + li) * LS + 32 * ks + 8 * lk;
+      const bf16x8 sh = ld8(&sS[0][bo]), sl = ld8(&sS[1][bo]);
+      X = mfma3(ops.kq[ks][0], ops.kq[ks][1], sh, sl, X);
+      Y = mfma3(ops.kq[ks][2], ops.kq[ks][3], sh, sl, Y);
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < D * DVT; idx += kNT) {
-    const int d = idx / DVT, e = idx - d * DVT;
-    Sg[(size_t)d * D + col0 + e] = sS[d * LDV + e];
+    load_kq(ops, cn);
+    // R = beta (V - e^gamma X) -> LDS;  O = e^gamma Y (inter-chunk part)
+    f32x4 O;
+    {
+      const int j = 16 * ocb + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const float r = sBeta[i] * (v4[e] - sEg[i] * X[e]);
+        O[e] = sEg[i] * Y[e];
+        __bf16 hi, lo;
+        split_bf16(r, hi, lo);
+        sR[0][j * LR + i] = hi;
+        sR[1][j * LR + i] = lo;
+      }
+    }
+    const float gl_cur = ops.glast;
+    (void)gl_cur;
+    load_misc(ops, cn);
+    __syncthreads();
+    // V' = Tm R for this wave's output block
+    f32x4 Vp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int bo = (16 * ocb + li) * LR + 32 * ks + 8 * lk;
+      Vp = mfma3(ops.tp[ks][0], ops.tp[ks][1], ld8(&sR[0][bo]), ld8(&sR[1][bo]), Vp);
+    }
+    __syncthreads();  // every wave is done reading R
+    {
+      const int j = 16 * ocb + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        __bf16 hi, lo;
+        split_bf16(Vp[e], hi, lo);
+        sV[0][j * LR + i] = hi;
+        sV[1][j * LR + i] = lo;
+        split_bf16(sDec[i] * Vp[e], hi, lo);
+        sR[0][j * LR + i] = hi;
+        sR[1][j * LR + i] = lo;
+      }
+    }
+    __syncthreads();
+    // O += P V'  and store the pre-norm output
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int bo = (16 * ocb + li) * LR + 32 * ks + 8 * lk;
+      O = mfma3(ops.tp[ks][2], ops.tp[ks][3], ld8(&sV[0][bo]), ld8(&sV[1][bo]), O);
+    }
+    load_tp(ops, cn);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      if (i < nc)
+        p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * ocb + li] = O[e];
+    }
+    // S <- e^{gamma_last} S + K^T (e^{gamma_last - gamma} V')
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+      if (!owns(q)) continue;
+      const int cb = (wave + kSW * q) % NCB;
+      S[q] *= egl;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+        S[q] = mfma3(ops.kt[q][ks][0], ops.kt[q][ks][1], ld8(&sR[0][bo]), ld8(&sR[1][bo]), S[q]);
+      }
+    }
+    load_kt(ops, cn);
   }
 
-  // final conv window = the last K raw inputs of [window ; tokens]; the v
-  // channels of head h, plus q/k channels of K-head m from its first V-head.
-  // Phase 1 (an earlier launch) has finished reading the old window.
-  if (blockIdx.z == 0) {
+#pragma unroll
+  for (int q = 0; q < SPW; ++q) {
+    if (!owns(q)) continue;
+    const int st = wave + kSW * q, rb = st / NCB, cb = st - rb * NCB;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li] = S[q][e];
+  }
+
+  // Final conv window = the last K raw inputs of [window ; tokens], for this
+  // tile's v channels, plus the q/k channels of K-head m from tile 0 of its
+  // first V-head.  No other workgroup reads these channels of the window
+  // (the prep kernel, an earlier launch, read the q/k ones).
+  __syncthreads();
+  {
+    const bool qk = blockIdx.z == 0 && h % p.r == 0;
+    const int nch = DVT + (qk ? 2 * D : 0);
+    const int vbase = 2 * p.Hk * D + h * D + col0;
     void* win = static_cast<char*>(p.conv) + (size_t)si.slot * K * p.C * io::bytes;
-    const int nch = (h % p.r == 0) ? 3 * D : D;
-    for (int e = tid; e < nch; e += kNT) {
-      const int ch = e < D ? 2 * p.Hk * D + h * D + e
-                   : e < 2 * D ? m * D + (e - D)
-                               : (p.Hk + m) * D + (e - 2 * D);
+    for (int e = tid; e < nch; e += kSNT) {
+      const int ch = e < DVT ? vbase + e
+                   : e < DVT + D ? m * D + (e - DVT)
+                                 : (p.Hk + m) * D + (e - DVT - D);
       float vals[K];
 #pragma unroll
       for (int j = 0; j < K; ++j) vals[j] = raw_input<Act, K>(p, si, (long long)si.len - K + j, ch);
@@ -415,117 +763,76 @@ __global__ __launch_bounds__(kNT) void prefill_state_kernel(PrefillParams p) {
   }
 }
 
-// ------------------------------------------------------------------ 3. output
+// ------------------------------------------------------------------ 3. norm
 
+// 256 threads = 8 token rows x 32 lanes; a lane owns D/32 consecutive values.
 template <typename Act, int D>
-__global__ __launch_bounds__(kNT) void prefill_output_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   using io = act_io<Act>;
-  constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NCT = D / 16;
-  __shared__ float sQ[kL * LDD];   // q_hat, then O
-  __shared__ float sK[kL * LDD];
-  __shared__ float sV[kL * LDD];   // V'
-  __shared__ float sP[kL * LDL];
-  __shared__ float sGam[kL];
-
+  constexpr int VPL = D / 32;      // values per lane
+  constexpr int ROWS = kNT / 32;   // rows per pass
   const int c = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
   if (t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
   const long long tok0 = si.begin + t0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, lk = lane >> 4;
-  if (si.slot < 0) {  // padding sequence: zero outputs
-    for (int idx = tid; idx < nc * D; idx += kNT) {
-      const int i = idx / D, d = idx - i * D;
-      const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d;
-      io::store(p.y, o, 0.f);
-      if (p.o_raw) p.o_raw[o] = 0.f;
-    }
-    return;
-  }
-  const int m = h / p.r;
-  for (int idx = tid; idx < kL * D; idx += kNT) {
-    const int i = idx / D, d = idx - i * D;
-    float qv = 0.f, kv = 0.f, vv = 0.f;
-    if (i < nc) {
-      const size_t o = ((size_t)(tok0 + i) * p.Hk + m) * D + d;
-      qv = p.s.qh[o];
-      kv = p.s.kh[o];
-      vv = p.s.u[((size_t)(tok0 + i) * p.Hv + h) * D + d];
-    }
-    sQ[i * LDD + d] = qv;
-    sK[i * LDD + d] = kv;
-    sV[i * LDD + d] = vv;
-  }
-  if (tid < kL) sGam[tid] = tid < nc ? p.s.gam[(size_t)(tok0 + tid) * p.Hv + h] : 0.f;
-  __syncthreads();
-
-  // P = mask_{j<=i}(e^{gamma_i - gamma_j}) * (Q K^T), block lower triangle
-  for (int t = wave; t < NTL * NTL; t += kNW) {
-    const int I = t / NTL, J = t - I * NTL;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (J <= I)
-      for (int k0 = 0; k0 < D; k0 += 4)
-        acc = mfma_f32(sQ[(16 * I + li) * LDD + k0 + lk], sK[(16 * J + li) * LDD + k0 + lk], acc);
+  const int tid = threadIdx.x, sub = tid & 31, rr = tid >> 5;
+  const int d0 = sub * VPL;
+  float nw[VPL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * I + 4 * lk + e, col = 16 * J + li;
-      sP[row * LDL + col] = col <= row ? acc[e] * expf(sGam[row] - sGam[col]) : 0.f;
-    }
-  }
-  __syncthreads();
-
-  // O = O_inter + P V'  (written over q_hat in LDS)
-  for (int t = wave; t < NTL * NCT; t += kNW) {
-    const int I = t / NCT, J = t - I * NCT;
-    f32x4 acc;
+  for (int k = 0; k < VPL; ++k) nw[k] = p.norm_w[d0 + k];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * I + 4 * lk + e;
-      acc[e] = row < nc ? p.s.oi[((size_t)(tok0 + row) * p.Hv + h) * D + 16 * J + li] : 0.f;
-    }
-    for (int k0 = 0; k0 < kL; k0 += 4)
-      acc = mfma_f32(sP[(16 * I + li) * LDL + k0 + lk], sV[(k0 + lk) * LDD + 16 * J + li], acc);
+  for (int pass = 0; pass < kL / ROWS; ++pass) {
+    const int i = pass * ROWS + rr;
+    const bool ok = i < nc;
+    const size_t o = ((size_t)(tok0 + (ok ? i : 0)) * p.Hv + h) * D + d0;
+    if (si.slot < 0) {  // padding sequence: zero outputs
+      if (ok)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sQ[(16 * I + 4 * lk + e) * LDD + 16 * J + li] = acc[e];
-  }
-  __syncthreads();
-
-  // gated RMSNorm per token
-  for (int i = wave; i < nc; i += kNW) {
+        for (int k = 0; k < VPL; ++k) {
+          io::store(p.y, o + k, 0.f);
+          p.obuf[o + k] = 0.f;
+        }
+      continue;
+    }
+    float ov[VPL], zv[VPL];
     float ss = 0.f;
-    for (int d = lane; d < D; d += 64) ss = fmaf(sQ[i * LDD + d], sQ[i * LDD + d], ss);
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
-    const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D;
-    for (int d = lane; d < D; d += 64) {
-      const float ov = sQ[i * LDD + d];
-      io::store(p.y, o + d, p.norm_w[d] * ov * inv * silu(io::load(p.z, o + d)));
-      if (p.o_raw) p.o_raw[o + d] = ov;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      ov[k] = ok ? p.obuf[o + k] : 0.f;
+      zv[k] = ok ? io::load(p.z, o + k) : 0.f;
+      ss = fmaf(ov[k], ov[k], ss);
     }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
+    if (ok)
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) io::store(p.y, o + k, nw[k] * ov[k] * inv * silu(zv[k]));
   }
 }
 
 // ------------------------------------------------------------------ launch
 
-template <typename Act, int D, int K>
+template <typename Act, int D, int DVT, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
-  constexpr int DVT = D < 32 ? D : 32;
+  prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
   if (max_chunks > 0)
     prefill_prep_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
-  prefill_state_kernel<Act, D, DVT, K><<<dim3(p.N, p.Hv, D / DVT), kNT, 0, st>>>(p);
+  prefill_state_kernel<Act, D, DVT, K><<<dim3(p.N, p.Hv, D / DVT), kSNT, 0, st>>>(p);
   if (max_chunks > 0)
-    prefill_output_kernel<Act, D><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
+    prefill_norm_kernel<Act, D><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <typename Act, int D>
 static hipError_t prefill_k(const PrefillParams& p, int K, int mc, hipStream_t st) {
+  constexpr int DVT = 32;
   switch (K) {
-    case 2: return prefill_run<Act, D, 2>(p, mc, st);
-    case 3: return prefill_run<Act, D, 3>(p, mc, st);
-    case 4: return prefill_run<Act, D, 4>(p, mc, st);
+    case 2: return prefill_run<Act, D, DVT, 2>(p, mc, st);
+    case 3: return prefill_run<Act, D, DVT, 3>(p, mc, st);
+    case 4: return prefill_run<Act, D, DVT, 4>(p, mc, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -553,7 +860,6 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
   p.a = a;
   p.b = b;
   p.y = y;
-  p.o_raw = o_raw;
   p.rec = pool.recurrent;
   p.conv = pool.conv;
   p.cu = cu_seqlens;
@@ -563,7 +869,8 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
   p.A_log = w.A_log;
   p.dt_bias = w.dt_bias;
   p.norm_w = w.norm_weight;
-  p.s = carve(g, total_tokens, scratch);
+  p.s = carve(g, total_tokens, N, scratch);
+  p.obuf = o_raw ? o_raw : p.s.o;
   p.T = total_tokens;
   p.N = N;
   p.Hk = g.num_k_heads;
