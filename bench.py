@@ -4,14 +4,14 @@
 
 Headline (`value`): batched decode at one rank's share of the heads, B = 16
 rows, Hk = 8, Hv = 16, dk = dv = 128, bf16 activations, f32 state, 64-slot
-pool.  One step = gdn_conv_update + gdn_decode_batch for the 16 rows of one
-layer.  Steps rotate over 16 layer replicas (pools, weights and inputs) so
+pool.  One step = gdn_decode_step (conv update, state update and gated
+RMSNorm in one launch) for the 16 rows of one layer.  Steps rotate over 16 layer replicas (pools, weights and inputs) so
 that every step streams its state from HBM rather than from the 256 MB
 last-level cache, as consecutive layers of a model do.
 
 Also reported on the same JSON line:
-  roofline      the decode kernel: algorithmic bytes per launch / its mean
-                duration from HIP events on the launch stream, against 8 TB/s;
+  roofline      the fused decode kernel: algorithmic bytes per launch / its
+                mean duration from HIP events on the launch stream, vs 8 TB/s;
   prefill       4096-token single-sequence prefill (Hk=8, Hv=16) and the
                 8-sequence packed varlen prefill (Hk=16, Hv=32): tokens/s and
                 algorithmic MFMA fraction;
@@ -45,8 +45,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -87,13 +87,6 @@ class DecodeLayer:
         self.b = _t(data["b"], act)
 
 
-def decode_bytes(geom, B, act_bytes):
-    """Algorithmic bytes of one gdn_decode_batch launch: the state tile read
-    and written once, the f32 conv outputs it consumes, z, a, b and y."""
-    C, Hv, dk, dv = geom.channels, geom.num_v_heads, geom.head_k_dim, geom.head_v_dim
-    return B * (8 * Hv * dk * dv + 4 * C + 2 * Hv * dv * act_bytes + 2 * Hv * act_bytes)
-
-
 def step_bytes(geom, B, act_bytes):
     """Algorithmic bytes of one decode step (conv update + decode) per layer:
     state read + write, conv window (K-1 columns read, K written), the token's
@@ -108,6 +101,9 @@ def step_bytes(geom, B, act_bytes):
 
 
 def bench_decode(args):
+    """The headline step, replayed from a HIP graph (one graph = one pass over
+    the layer replicas), as the pages' serving path replays captured decode
+    steps.  An eager (one Python launch per step) figure is reported beside it."""
     import numpy as np
     import torch
 
@@ -120,41 +116,62 @@ def bench_decode(args):
                         s.conv_kernel, s.act)
     act = torch.bfloat16
     B = len(work.data["slot_idx"])
-    layers = [DecodeLayer(gdn, geom, work.data, act) for _ in range(args.replicas)]
-    qkv = torch.empty(B, geom.channels, device="cuda")
+    R = args.replicas
+    layers = [DecodeLayer(gdn, geom, work.data, act) for _ in range(R)]
     y = torch.empty(B, geom.num_v_heads, geom.head_v_dim, device="cuda", dtype=act)
+
+    def step(i, stream):
+        L = layers[i % R]
+        gdn.gdn_decode_step(geom, L.w, L.pool, L.slot, L.x, L.z, L.a, L.b, y, stream=stream)
+
     stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        L = layers[i % len(layers)]
-        gdn.gdn_conv_update(geom, L.w, L.pool, L.slot, L.x, qkv, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        gdn.gdn_decode_batch(geom, L.w, L.pool, L.slot, qkv, L.z, L.a, L.b, y, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-
     for i in range(args.warmup):
-        step(i)
+        step(i, stream)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # eager: one Python-side launch per step
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(i, stream)
+    torch.cuda.synchronize()
+    eager_dt = time.perf_counter() - t0
+
+    # graph: R steps (one per replica) captured once, replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(R):
+                step(i, side)
+    stream.wait_stream(side)
+    for _ in range(max(1, args.warmup // R)):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // R)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    t0 = time.perf_counter()
+    for k in range(reps):
+        evs[k][0].record(stream)
+        graph.replay()
+        evs[k][1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    per_launch = decode_bytes(geom, B, 2)
-    achieved = per_launch / (kern_ms * 1e-3)
+    nsteps = reps * R
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / R
+    per_launch = step_bytes(geom, B, 2)
+    achieved = per_launch / (launch_ms * 1e-3)
     return dict(
-        tokens_per_s=B * args.steps / dt, ms_per_step=dt * 1e3 / args.steps, B=B,
+        tokens_per_s=B * nsteps / dt, ms_per_step=dt * 1e3 / nsteps, steps=nsteps, B=B,
         workload=work.name, geom=geom,
+        eager={"tokens_per_s": B * args.steps / eager_dt,
+               "ms_per_step": eager_dt * 1e3 / args.steps},
         roofline={"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                   "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
-                  "kernel": "gdn::decode_kernel<bf16, 128, 256>",
-                  "bytes_per_launch": per_launch, "mean_launch_us": kern_ms * 1e3},
-        step_hbm_frac=step_bytes(geom, B, 2) / (dt / args.steps) / HBM_PEAK)
+                  "kernel": "gdn::decode_step_kernel<__bf16, 128, 2, 4>",
+                  "bytes_per_launch": per_launch, "mean_launch_us": launch_ms * 1e3,
+                  "timing": "HIP events around graph replays of 16 back-to-back launches"},
+        step_hbm_frac=per_launch / (dt / nsteps) / HBM_PEAK)
 
 
 # ------------------------------------------------------------------ prefill
@@ -253,7 +270,6 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
     z = torch.randn(B, s.num_v_heads, s.head_v_dim, device="cuda", generator=gen).to(act)
     a = torch.randn(B, s.num_v_heads, device="cuda", generator=gen).to(act)
     b = torch.randn(B, s.num_v_heads, device="cuda", generator=gen).to(act)
-    qkv = torch.empty(B, C, device="cuda")
     y = torch.empty(B, s.num_v_heads, s.head_v_dim, device="cuda", dtype=act)
     stream = torch.cuda.current_stream()
     pools = [L["pool"] for L in Ls]
@@ -276,9 +292,8 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
                 live = np.concatenate([new_slots, admitted]).astype(np.int32)
                 slot_d = _t(live, torch.int32)
             for L in Ls:
-                gdn.gdn_conv_update(geom, L["w"], L["pool"], slot_d, x, qkv, stream=stream)
-                gdn.gdn_decode_batch(geom, L["w"], L["pool"], slot_d, qkv, z, a, b, y,
-                                     stream=stream)
+                gdn.gdn_decode_step(geom, L["w"], L["pool"], slot_d, x, z, a, b, y,
+                                    stream=stream)
         return live
 
     live = run(2, live)
@@ -350,13 +365,15 @@ def main():
     dec = bench_decode(args)
     line = {
         "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+        "steps": dec["steps"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": dec["workload"], "rows": dec["B"], "num_k_heads": 8,
                    "num_v_heads": 16, "head_dim": 128, "conv_kernel": 4, "pool_slots": 64,
                    "activations": "bf16", "state": "f32",
-                   "cold_cache": f"{args.replicas} rotating layer replicas"},
+                   "cold_cache": f"{args.replicas} rotating layer replicas",
+                   "launch": "HIP graph replay"},
+        "eager": dec["eager"],
         "step_hbm_frac_algorithmic": dec["step_hbm_frac"],
         "roofline": dec["roofline"],
     }

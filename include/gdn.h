@@ -159,6 +159,18 @@ int gdn_decode_batch(const gdn_geometry* geom, const gdn_layer_weights* w,
                      const void* z, const void* a, const void* b, void* y,
                      float* o_raw, void* stream);
 
+/* Fused decode step: gdn_conv_update followed by gdn_decode_batch for the
+ * same rows, in one launch and without the f32 conv-output round trip (the
+ * batched decode chain of pegainfer issue #1001, Splits, with the conv and
+ * the state update of one layer in a single kernel).  Arguments as in those
+ * two calls; qkv_in [B][C] act.  Results equal the two-call sequence.
+ * Compiled for Hv/Hk in {1, 2, 4}; otherwise GDN_E_UNSUPPORTED. */
+int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
+                    const gdn_state_pool* pool, const int32_t* slot_idx,
+                    const int32_t* slot_idx_host, int32_t B, const void* qkv_in,
+                    const void* z, const void* a, const void* b, void* y,
+                    float* o_raw, void* stream);
+
 /* ------------------------------------------------------------- prefill */
 
 /* Chunkwise prefill of N packed sequences (pegainfer PR #1003, PR body,

@@ -18,7 +18,7 @@ from ._abi import GDN_BF16, GDN_F32, GdnError
 
 __all__ = ["Geometry", "LayerWeights", "StatePool", "GdnError", "gdn_slot_bytes",
            "gdn_prefill_scratch_bytes", "gdn_conv_update", "gdn_decode_batch",
-           "gdn_prefill_chunked", "gdn_state_compact", "library"]
+           "gdn_decode_step", "gdn_prefill_chunked", "gdn_state_compact", "library"]
 
 
 def library():
@@ -159,6 +159,25 @@ def gdn_decode_batch(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx:
         ctypes.byref(g), ctypes.byref(w.c), ctypes.byref(pool.c),
         _ptr(slot_idx, torch.int32, B, "slot_idx"), host, B,
         _ptr(qkv, torch.float32, B * geom.channels, "qkv"),
+        _ptr(z, act, B * Hv * dv, "z"), _ptr(a, act, B * Hv, "a"), _ptr(b, act, B * Hv, "b"),
+        _ptr(y, act, B * Hv * dv, "y"), _ptr(o_raw, torch.float32, B * Hv * dv, "o_raw"),
+        _stream(stream)))
+
+
+def gdn_decode_step(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx: torch.Tensor,
+                    qkv_in: torch.Tensor, z: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                    y: torch.Tensor, o_raw: torch.Tensor | None = None, slot_idx_host=None,
+                    stream=None) -> None:
+    lib = _abi.load()
+    B = slot_idx.numel()
+    Hv, dv = geom.num_v_heads, geom.head_v_dim
+    act = geom.act_dtype
+    _, host = _host_i32(slot_idx_host, B, "slot_idx_host")
+    g = geom.c()
+    _abi.check(lib.gdn_decode_step(
+        ctypes.byref(g), ctypes.byref(w.c), ctypes.byref(pool.c),
+        _ptr(slot_idx, torch.int32, B, "slot_idx"), host, B,
+        _ptr(qkv_in, act, B * geom.channels, "qkv_in"),
         _ptr(z, act, B * Hv * dv, "z"), _ptr(a, act, B * Hv, "a"), _ptr(b, act, B * Hv, "b"),
         _ptr(y, act, B * Hv * dv, "y"), _ptr(o_raw, torch.float32, B * Hv * dv, "o_raw"),
         _stream(stream)))

@@ -70,6 +70,8 @@ PROTOTYPES = {
     "gdn_conv_update": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _I32, _P, _P, _P]),
     "gdn_decode_batch": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _I32, _P, _P, _P, _P, _P,
                                         _P, _P]),
+    "gdn_decode_step": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
+                                       _P]),
     "gdn_prefill_chunked": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _P, _P, _P, _I32, _P, _P,
                                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "gdn_state_compact": (ctypes.c_int, [_GP, _PP, _I32, _P, _P, _P, _P, _I32, _P]),

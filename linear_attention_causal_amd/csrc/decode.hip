@@ -233,6 +233,281 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   }
 }
 
+// ------------------------------------------------------------- fused step
+
+struct StepParams {
+  const void* x;        // [B][C] act (fused [q|k|v] input of this token)
+  const void* weight;   // [C][K] act
+  void* conv;           // [P][K][C] act
+  const void* z;        // [B][Hv][dv] act
+  const void* a;        // [B][Hv] act
+  const void* b;        // [B][Hv] act
+  void* y;              // [B][Hv][dv] act
+  float* o_raw;         // [B][Hv][dv] f32 or null
+  float* rec;           // [P][Hv][D][D] f32
+  const int32_t* slot_idx;
+  const float* A_log;
+  const float* dt_bias;
+  const float* norm_w;
+  int B, Hk, Hv, C, num_slots;
+  float l2eps, rmseps, scale;
+};
+
+// One workgroup per (row, K-head): the conv of the K-head's q/k channels and
+// of the v channels of its R V-heads (so every conv-window channel has one
+// owner), then R independent state steps on groups of HT = 2D threads.
+// Order of work inside a group, chosen so that HBM is busy throughout:
+//   1. the small conv inputs are requested first, then the state tile in two
+//      column halves (A then B);
+//   2. conv + SiLU, l2 norms and gates run while the tile streams in;
+//   3. half A is reduced (kappa = S^T k, rho = S^T q), updated and stored
+//      while half B's loads are still arriving; then half B;
+//   4. gated RMSNorm over both halves' outputs.
+template <typename Act, int D, int R, int K>
+__global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
+  using io = act_io<Act>;
+  constexpr int HT = 2 * D;          // threads per V-head
+  constexpr int NT = HT * R;
+  constexpr int CGH = D / 8;         // four-column groups per half
+  constexpr int RG = HT / CGH;       // row groups (16)
+  constexpr int RPT = D / RG;        // rows per thread per half
+  constexpr int HW = HT / 64;        // waves per V-head
+  constexpr int NCH = (2 + R) * D;   // channels this workgroup convolves
+  constexpr int CPT = (NCH + NT - 1) / NT;
+  static_assert(HT % 64 == 0 && RG == 16 && CGH <= 64, "layout");
+
+  __shared__ float s_x[NCH];         // conv + SiLU output: q, k, v_0 .. v_{R-1}
+  __shared__ f32x4 s_red[R][2][HW][2][CGH];
+
+  const int tid = threadIdx.x;
+  const int grp = tid / HT, gt = tid - grp * HT;   // V-head within the K-head, thread in group
+  const int lane = tid & 63, gwave = gt >> 6;
+  const int cgh = gt % CGH, rg = gt / CGH;
+  const int row = blockIdx.x / p.Hk;
+  const int m = blockIdx.x - row * p.Hk;
+  const int h = m * R + grp;
+  const size_t out_off = ((size_t)row * p.Hv + h) * D;
+  const int slot = p.slot_idx[row];
+  if (slot < 0 || slot >= p.num_slots) {  // padding row: zeros, no state access
+    for (int j = gt; j < D; j += HT) {
+      io::store(p.y, out_off + j, 0.f);
+      if (p.o_raw) p.o_raw[out_off + j] = 0.f;
+    }
+    return;
+  }
+
+  // 1. conv inputs (window columns 1..K-1, the token, the weights), then the tile
+  void* win = static_cast<char*>(p.conv) + (size_t)slot * K * p.C * io::bytes;
+  float col[CPT][K], wt[CPT][K];
+  int chs[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int e = tid + q * NT;
+    const int ee = e < NCH ? e : 0;
+    const int part = ee / D, j = ee - part * D;
+    chs[q] = part == 0 ? m * D + j
+           : part == 1 ? (p.Hk + m) * D + j
+                       : 2 * p.Hk * D + (m * R + part - 2) * D + j;
+#pragma unroll
+    for (int k = 1; k < K; ++k) col[q][k - 1] = io::load(win, (size_t)k * p.C + chs[q]);
+    col[q][K - 1] = io::load(p.x, (size_t)row * p.C + chs[q]);
+#pragma unroll
+    for (int k = 0; k < K; ++k) wt[q][k] = io::load(p.weight, (size_t)chs[q] * K + k);
+  }
+  const float a_in = io::load(p.a, (size_t)row * p.Hv + h);
+  const float b_in = io::load(p.b, (size_t)row * p.Hv + h);
+  float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
+  f32x4 s[2][RPT];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      s[hf][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+          S + (size_t)(rg + RG * i) * D + hf * (D / 2) + 4 * cgh));
+
+  // 2. conv + SiLU; shifted window written back (raw inputs: lossless)
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int e = tid + q * NT;
+    if (e < NCH) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc = fmaf(wt[q][k], col[q][k], acc);
+      s_x[e] = silu(acc);
+#pragma unroll
+      for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chs[q], col[q][k]);
+    }
+  }
+  float g, beta;
+  gates(p.A_log[h], p.dt_bias[h], a_in, b_in, g, beta);
+  const float eg = expf(g);
+  __syncthreads();
+
+  const float* sq = s_x;
+  const float* sk = s_x + D;
+  const float* sv = s_x + (2 + grp) * D;
+  float sqq = 0.f, skk = 0.f, sqk = 0.f;
+  for (int j = lane; j < D; j += 64) {
+    const float qv = sq[j], kv = sk[j];
+    sqq = fmaf(qv, qv, sqq);
+    skk = fmaf(kv, kv, skk);
+    sqk = fmaf(qv, kv, sqk);
+  }
+  sqq = wave_sum(sqq);
+  skk = wave_sum(skk);
+  sqk = wave_sum(sqk);
+  const float rq = p.scale / sqrtf(sqq + p.l2eps);
+  const float rk = 1.0f / sqrtf(skk + p.l2eps);
+  const float kq = sqk * rq * rk;
+  float kr[RPT], qr[RPT];   // k_hat, q_hat at this thread's rows
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    kr[i] = sk[rg + RG * i] * rk;
+    qr[i] = sq[rg + RG * i] * rq;
+  }
+
+  // 3. per column half: reduce, update, store
+  f32x4 o[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      kap += s[hf][i] * kr[i];
+      rho += s[hf][i] * qr[i];
+    }
+#pragma unroll
+    for (int off = CGH; off < 64; off <<= 1) {
+      kap.x += __shfl_xor(kap.x, off, 64); kap.y += __shfl_xor(kap.y, off, 64);
+      kap.z += __shfl_xor(kap.z, off, 64); kap.w += __shfl_xor(kap.w, off, 64);
+      rho.x += __shfl_xor(rho.x, off, 64); rho.y += __shfl_xor(rho.y, off, 64);
+      rho.z += __shfl_xor(rho.z, off, 64); rho.w += __shfl_xor(rho.w, off, 64);
+    }
+    if (lane < CGH) {
+      s_red[grp][hf][gwave][0][cgh] = kap;
+      s_red[grp][hf][gwave][1][cgh] = rho;
+    }
+    __syncthreads();
+    kap = s_red[grp][hf][0][0][cgh];
+    rho = s_red[grp][hf][0][1][cgh];
+#pragma unroll
+    for (int w = 1; w < HW; ++w) {
+      kap += s_red[grp][hf][w][0][cgh];
+      rho += s_red[grp][hf][w][1][cgh];
+    }
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[hf * (D / 2) + 4 * cgh]);
+    const f32x4 u = beta * (v - eg * kap);
+    o[hf] = eg * rho + u * kq;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      f32x4 ns;
+      ns.x = fmaf(eg, s[hf][i].x, kr[i] * u.x);
+      ns.y = fmaf(eg, s[hf][i].y, kr[i] * u.y);
+      ns.z = fmaf(eg, s[hf][i].z, kr[i] * u.z);
+      ns.w = fmaf(eg, s[hf][i].w, kr[i] * u.w);
+      __builtin_nontemporal_store(
+          ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + hf * (D / 2) + 4 * cgh));
+    }
+  }
+
+  // 4. gated RMSNorm over the D outputs of this head (first wave of the group;
+  // every row group holds all columns, so the xor-reduction over the CGH
+  // lanes of a row group yields the full sum)
+  if (gwave == 0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      ss += o[hf].x * o[hf].x + o[hf].y * o[hf].y + o[hf].z * o[hf].z + o[hf].w * o[hf].w;
+#pragma unroll
+    for (int off = 1; off < CGH; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
+    if (lane < CGH) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c0 = hf * (D / 2) + 4 * cgh;
+        const f32x4 nw = *reinterpret_cast<const f32x4*>(p.norm_w + c0);
+        const f32x4 zz = io::load4(p.z, out_off + c0);
+        f32x4 yv;
+        yv.x = nw.x * o[hf].x * inv * silu(zz.x);
+        yv.y = nw.y * o[hf].y * inv * silu(zz.y);
+        yv.z = nw.z * o[hf].z * inv * silu(zz.z);
+        yv.w = nw.w * o[hf].w * inv * silu(zz.w);
+        io::store4(p.y, out_off + c0, yv);
+        if (p.o_raw) *reinterpret_cast<f32x4*>(p.o_raw + out_off + c0) = o[hf];
+      }
+    }
+  }
+}
+
+template <typename Act, int D, int R>
+static hipError_t step_k(const StepParams& p, int K, hipStream_t st) {
+  dim3 grid(p.B * p.Hk);
+  constexpr int NT = 2 * D * R;
+  switch (K) {
+    case 2: decode_step_kernel<Act, D, R, 2><<<grid, NT, 0, st>>>(p); break;
+    case 3: decode_step_kernel<Act, D, R, 3><<<grid, NT, 0, st>>>(p); break;
+    case 4: decode_step_kernel<Act, D, R, 4><<<grid, NT, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename Act, int D>
+static hipError_t step_r(const StepParams& p, int R, int K, hipStream_t st) {
+  switch (R) {
+    case 1: return step_k<Act, D, 1>(p, K, st);
+    case 2: return step_k<Act, D, 2>(p, K, st);
+    case 4: return step_k<Act, D, 4>(p, K, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename Act>
+static hipError_t step_d(const StepParams& p, int D, int R, int K, hipStream_t st) {
+  switch (D) {
+    case 32: return step_r<Act, 32>(p, R, K, st);
+    case 64: return step_r<Act, 64>(p, R, K, st);
+    case 128: return step_r<Act, 128>(p, R, K, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_step_supported(const gdn_geometry& g) {
+  const int r = g.num_v_heads / g.num_k_heads;
+  return r == 1 || r == 2 || r == 4;
+}
+
+hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
+                              const gdn_state_pool& pool, const int32_t* slot_idx, int B,
+                              const void* qkv_in, const void* z, const void* a, const void* b,
+                              void* y, float* o_raw, hipStream_t stream) {
+  StepParams p;
+  p.x = qkv_in;
+  p.weight = w.conv_weight;
+  p.conv = pool.conv;
+  p.z = z;
+  p.a = a;
+  p.b = b;
+  p.y = y;
+  p.o_raw = o_raw;
+  p.rec = pool.recurrent;
+  p.slot_idx = slot_idx;
+  p.A_log = w.A_log;
+  p.dt_bias = w.dt_bias;
+  p.norm_w = w.norm_weight;
+  p.B = B;
+  p.Hk = g.num_k_heads;
+  p.Hv = g.num_v_heads;
+  p.C = 2 * g.num_k_heads * g.head_k_dim + g.num_v_heads * g.head_v_dim;
+  p.num_slots = pool.num_slots;
+  p.l2eps = g.l2norm_eps;
+  p.rmseps = g.rmsnorm_eps;
+  p.scale = g.scale > 0.f ? g.scale : 1.0f / sqrtf((float)g.head_k_dim);
+  const int R = g.num_v_heads / g.num_k_heads;
+  if (g.act_dtype == GDN_BF16) return step_d<__bf16>(p, g.head_k_dim, R, g.conv_kernel, stream);
+  return step_d<float>(p, g.head_k_dim, R, g.conv_kernel, stream);
+}
+
 // ------------------------------------------------------------- launchers
 
 template <typename Act>

@@ -18,6 +18,13 @@ hipError_t launch_decode(const gdn_geometry& g, const gdn_layer_weights& w,
                          const float* qkv, const void* z, const void* a,
                          const void* b, void* y, float* o_raw, hipStream_t stream);
 
+bool decode_step_supported(const gdn_geometry& g);
+
+hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
+                              const gdn_state_pool& pool, const int32_t* slot_idx, int B,
+                              const void* qkv_in, const void* z, const void* a, const void* b,
+                              void* y, float* o_raw, hipStream_t stream);
+
 // Token-indexed scratch layout of the chunkwise prefill (see prefill.hip).
 size_t prefill_scratch_bytes(const gdn_geometry& g, long long total_tokens,
                              long long num_seqs);

@@ -34,7 +34,7 @@ def host_i32(vals):
 
 def test_exports_every_declared_function():
     names = _abi.header_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
     assert set(_abi.PROTOTYPES) == set(names)

@@ -150,3 +150,41 @@ def test_decode_repeated_steps_match_oracle():
                                  inp["a"], inp["b"])
         assert_close(f"y step {step}", maxrel_heads(host(y), yo), y_tol(s))
     assert_close("state", maxrel_states(host(P.rec)[slots], S[slots]), TOL_F32)
+
+
+@pytest.mark.parametrize("s,B,P", [(wl.TINY, 3, 5), (wl.RANK_LOCAL, 16, 64),
+                                   (wl.FULL_HEADS, 64, 80), (wl.Shape(4, 16, 64, 64, 3, "bf16"), 5, 9),
+                                   (wl.Shape(4, 4, 64, 64, 2, "bf16"), 6, 8)])
+def test_fused_decode_step_matches_oracle_and_two_calls(s, B, P):
+    """gdn_decode_step (conv + state step + gated norm in one launch) against
+    the oracle, and against gdn_conv_update + gdn_decode_batch on a copy of
+    the same pools; a padding row included."""
+    import linear_attention_causal_amd as gdn
+    from gpu_helpers import act_dtype, dev
+    work = wl.decode_batch(seed=12, B=B, P=P, s=s)
+    d = work.data
+    slots = d["slot_idx"].copy()
+    slots[B // 2] = -1
+    L = Layer(s, d["weights"])
+    P1, P2 = Pool(s, d["rec"], d["conv"]), Pool(s, d["rec"], d["conv"])
+    ad = act_dtype(s)
+    y1 = torch.empty(B, s.num_v_heads, s.head_v_dim, device="cuda", dtype=ad)
+    o1 = torch.empty(B, s.num_v_heads, s.head_v_dim, device="cuda")
+    gdn.gdn_decode_step(L.geom, L.w, P1.pool, dev(slots, torch.int32), dev(d["x"], ad),
+                        dev(d["z"], ad), dev(d["a"], ad), dev(d["b"], ad), y1, o1,
+                        slot_idx_host=slots)
+    y2, o2 = decode_step(L, P2, slots, d["x"], d["z"], d["a"], d["b"])
+    torch.cuda.synchronize()
+    assert not host(y1)[B // 2].any()
+    np.testing.assert_allclose(host(o1), host(o2), rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(host(P1.rec), host(P2.rec), rtol=1e-5, atol=1e-6)
+    np.testing.assert_array_equal(host(P1.conv), host(P2.conv))
+    keep = np.array([i for i in range(B) if slots[i] >= 0])
+    yo, oo, S, W = _oracle_decode(L, d["rec"], d["conv"], slots[keep],
+                                  {k: d[k][keep] for k in ("x", "z", "a", "b")})
+    assert_close("y", maxrel_heads(host(y1)[keep], yo), y_tol(s))
+    assert_close("o_raw", maxrel_heads(host(o1)[keep], oo), TOL_F32)
+    assert_close("state", maxrel_states(host(P1.rec)[slots[keep]], S[slots[keep]]), TOL_F32)
+    np.testing.assert_array_equal(host(P1.conv)[slots[keep]], W[slots[keep]])
+    untouched = np.setdiff1d(np.arange(P), slots[keep])
+    np.testing.assert_array_equal(host(P1.rec)[untouched], d["rec"][untouched])
