@@ -230,7 +230,7 @@ def bench_prefill(work, iters, replicas):
             "algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
             "mfma_frac_of_bf16_peak": flops / (ms * 1e-3) / BF16_PEAK,
             "mfma_frac_of_f32_peak": flops / (ms * 1e-3) / F32_MFMA_PEAK,
-            "mfma_dtype": "f32", "kernels": 3}
+            "mfma_dtype": "bf16 x3 (hi/lo split operands, f32 accumulate)", "kernels": 4}
 
 
 # ------------------------------------------------------------------ serving

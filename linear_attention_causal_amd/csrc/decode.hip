@@ -136,8 +136,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
   f32x4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    s[i] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg + RG * i) * D + 4 * cg);
+  for (int i = 0; i < RPT; ++i)  // streamed once: nontemporal
+    s[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(S + (size_t)(rg + RG * i) * D + 4 * cg));
 
   float g, beta;
   gates(p.A_log[h], p.dt_bias[h], io::load(p.a, (size_t)row * p.Hv + h),
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     ns.y = fmaf(eg, s[i].y, kk * u.y);
     ns.z = fmaf(eg, s[i].z, kk * u.z);
     ns.w = fmaf(eg, s[i].w, kk * u.w);
-    *reinterpret_cast<f32x4*>(S + (size_t)r_ * D + 4 * cg) = ns;
+    __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + (size_t)r_ * D + 4 * cg));
   }
 
   // gated RMSNorm over the D outputs of this head (wave 0; every row group
@@ -257,27 +258,32 @@ struct StepParams {
 // of the v channels of its R V-heads (so every conv-window channel has one
 // owner), then R independent state steps on groups of HT = 2D threads.
 // Order of work inside a group, chosen so that HBM is busy throughout:
-//   1. the small conv inputs are requested first, then the state tile in two
-//      column halves (A then B);
+//   1. the small conv inputs are requested first, then the state tile in NQ
+//      column chunks;
 //   2. conv + SiLU, l2 norms and gates run while the tile streams in;
-//   3. half A is reduced (kappa = S^T k, rho = S^T q), updated and stored
-//      while half B's loads are still arriving; then half B;
-//   4. gated RMSNorm over both halves' outputs.
+//   3. chunk 0 is reduced (kappa = S^T k, rho = S^T q), updated and stored
+//      while the later chunks' loads are still arriving; then chunk 1, ...;
+//   4. gated RMSNorm over all chunks' outputs.
+constexpr int kDecodeChunks = 1;   // column chunks of the state tile (NQ)
+constexpr int kStepThreadsPerDim = 2;  // threads per V-head = this * D
+
 template <typename Act, int D, int R, int K>
-__global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
+__global__ __launch_bounds__(kStepThreadsPerDim * D * R) void decode_step_kernel(StepParams p) {
   using io = act_io<Act>;
-  constexpr int HT = 2 * D;          // threads per V-head
+  constexpr int NQ = kDecodeChunks;
+  constexpr int HT = kStepThreadsPerDim * D;   // threads per V-head
   constexpr int NT = HT * R;
-  constexpr int CGH = D / 8;         // four-column groups per half
-  constexpr int RG = HT / CGH;       // row groups (16)
-  constexpr int RPT = D / RG;        // rows per thread per half
+  constexpr int CW = D / NQ;         // columns per chunk
+  constexpr int CGH = CW / 4;        // four-column groups per chunk
+  constexpr int RG = HT / CGH;       // row groups
+  constexpr int RPT = D / RG;        // rows per thread per chunk
   constexpr int HW = HT / 64;        // waves per V-head
   constexpr int NCH = (2 + R) * D;   // channels this workgroup convolves
   constexpr int CPT = (NCH + NT - 1) / NT;
-  static_assert(HT % 64 == 0 && RG == 16 && CGH <= 64, "layout");
+  static_assert(HT % 64 == 0 && CGH <= 64 && 64 % CGH == 0 && RPT >= 1, "layout");
 
   __shared__ float s_x[NCH];         // conv + SiLU output: q, k, v_0 .. v_{R-1}
-  __shared__ f32x4 s_red[R][2][HW][2][CGH];
+  __shared__ f32x4 s_red[R][NQ][HW][2][CGH];
 
   const int tid = threadIdx.x;
   const int grp = tid / HT, gt = tid - grp * HT;   // V-head within the K-head, thread in group
@@ -317,13 +323,13 @@ __global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
   const float a_in = io::load(p.a, (size_t)row * p.Hv + h);
   const float b_in = io::load(p.b, (size_t)row * p.Hv + h);
   float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
-  f32x4 s[2][RPT];
+  f32x4 s[NQ][RPT];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+  for (int hf = 0; hf < NQ; ++hf)
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       s[hf][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-          S + (size_t)(rg + RG * i) * D + hf * (D / 2) + 4 * cgh));
+          S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
 
   // 2. conv + SiLU; shifted window written back (raw inputs: lossless)
 #pragma unroll
@@ -366,10 +372,10 @@ __global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
     qr[i] = sq[rg + RG * i] * rq;
   }
 
-  // 3. per column half: reduce, update, store
-  f32x4 o[2];
+  // 3. per column chunk: reduce, update, store
+  f32x4 o[NQ];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int hf = 0; hf < NQ; ++hf) {
     f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
       kap += s_red[grp][hf][w][0][cgh];
       rho += s_red[grp][hf][w][1][cgh];
     }
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[hf * (D / 2) + 4 * cgh]);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[hf * CW + 4 * cgh]);
     const f32x4 u = beta * (v - eg * kap);
     o[hf] = eg * rho + u * kq;
 #pragma unroll
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
       ns.z = fmaf(eg, s[hf][i].z, kr[i] * u.z);
       ns.w = fmaf(eg, s[hf][i].w, kr[i] * u.w);
       __builtin_nontemporal_store(
-          ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + hf * (D / 2) + 4 * cgh));
+          ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
     }
   }
 
@@ -416,15 +422,15 @@ __global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
   if (gwave == 0) {
     float ss = 0.f;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int hf = 0; hf < NQ; ++hf)
       ss += o[hf].x * o[hf].x + o[hf].y * o[hf].y + o[hf].z * o[hf].z + o[hf].w * o[hf].w;
 #pragma unroll
     for (int off = 1; off < CGH; off <<= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
     if (lane < CGH) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int c0 = hf * (D / 2) + 4 * cgh;
+      for (int hf = 0; hf < NQ; ++hf) {
+        const int c0 = hf * CW + 4 * cgh;
         const f32x4 nw = *reinterpret_cast<const f32x4*>(p.norm_w + c0);
         const f32x4 zz = io::load4(p.z, out_off + c0);
         f32x4 yv;
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(2 * D * R) void decode_step_kernel(StepParams p) {
 template <typename Act, int D, int R>
 static hipError_t step_k(const StepParams& p, int K, hipStream_t st) {
   dim3 grid(p.B * p.Hk);
-  constexpr int NT = 2 * D * R;
+  constexpr int NT = kStepThreadsPerDim * D * R;
   switch (K) {
     case 2: decode_step_kernel<Act, D, R, 2><<<grid, NT, 0, st>>>(p); break;
     case 3: decode_step_kernel<Act, D, R, 3><<<grid, NT, 0, st>>>(p); break;
