@@ -35,8 +35,8 @@
  *     runs asynchronously.
  *   - Return 0 (GDN_OK) on success or a negative GDN_E_* code.  Every check
  *     happens before anything is enqueued: on error no kernel runs and no
- *     memory changes ("fails closed", pegainfer PR #1003, PR body, config
- *     bullet).  gdn_last_error() gives a message for the calling thread.
+ *     memory changes (the pages' engines likewise reject a bad head split up
+ *     front: pegainfer PR #1003, PR body, config bullet).  gdn_last_error() gives a message for the calling thread.
  *   - Layouts are dense, row-major, innermost index last.  C = 2*Hk*dk +
  *     Hv*dv channels in [q | k | v] order, head-major inside each region.
  *   - "act" arrays use geometry.act_dtype (GDN_F32 or GDN_BF16).
@@ -93,8 +93,8 @@ typedef struct {
 } gdn_geometry;
 
 /* Per-layer weights, device.  norm_weight is one [dv] vector shared by all
- * V-heads ("norm_weight kept replicated (head-shared)", pegainfer PR #1003,
- * PR body, weights bullet). */
+ * V-heads (the norm weight is replicated, not sharded, across ranks:
+ * pegainfer PR #1003, PR body, weights bullet). */
 typedef struct {
   const void* conv_weight;  /* [C][K] act: depthwise conv1d weight, tap K-1
                                multiplies the current token, no bias */
@@ -116,8 +116,8 @@ typedef struct {
 /* ------------------------------------------------------------- sizes */
 
 /* Bytes of one slot in the recurrent pool and in the conv pool, for the
- * caller's capacity math ("capacity math derives from local
- * allocation_bytes", pegainfer PR #1003, PR body, tp_executor bullet). */
+ * caller's capacity math (the pages size worker capacity from these
+ * rank-local byte counts: pegainfer PR #1003, PR body, tp_executor bullet). */
 int gdn_slot_bytes(const gdn_geometry* geom, size_t* recurrent_bytes,
                    size_t* conv_bytes);
 
@@ -137,8 +137,8 @@ int gdn_prefill_scratch_bytes(const gdn_geometry* geom, int32_t total_tokens,
  * qkv_in  [B][C] act;  qkv_out [B][C] f32 (consumed by gdn_decode_batch).
  * slot_idx [B] int32 device; slot_idx_host: optional host copy, validated
  * (range, duplicates) when given.  B == 0 is a no-op.
- * (pegainfer issue #1001, Splits: "GDR decode/conv" chains of pegainfer
- * PR #1003 run on slot-indexed conv state.) */
+ * (the decode-time conv of the layer on slot-indexed conv state:
+ * pegainfer issue #1001, Splits; pegainfer PR #1003, PR body.) */
 int gdn_conv_update(const gdn_geometry* geom, const gdn_layer_weights* w,
                     const gdn_state_pool* pool, const int32_t* slot_idx,
                     const int32_t* slot_idx_host, int32_t B,

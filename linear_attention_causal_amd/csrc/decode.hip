@@ -2,8 +2,8 @@
 //
 //   conv_update_kernel  slot-indexed conv window shift + depthwise conv + SiLU
 //                       over the fused [q|k|v] channels (pegainfer PR #1003,
-//                       PR body: the "GDR decode/conv" chain on slot-indexed
-//                       conv state).
+//                       PR body: the decode-time conv of the layer on
+//                       slot-indexed conv state).
 //   decode_kernel       per (row, V-head): l2norm of q/k, softplus gates, one
 //                       read-modify-write pass over the f32 state tile
 //                       S[dk][dv], and the gated RMSNorm epilogue (pegainfer

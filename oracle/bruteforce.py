@@ -9,7 +9,7 @@ Written separately from gdn_oracle.c so that the two can check each other:
     with explicit dk x dk matrices, which is the gated delta rule
     S_t = e^{g_t} S_{t-1} + beta_t k_t (v_t - e^{g_t} S_{t-1}^T k_t)^T
     multiplied out (Yang, Kautz & Hatamizadeh, "Gated Delta Networks",
-    ICLR 2025; the "delta-rule loop" of cortex commit 95dc874,
+    ICLR 2025; the per-V-head delta-rule state of cortex commit 95dc874,
     TpQwen3_5GatedDeltaNet bullet);
   * the gates and norms are written from their closed forms.
 """

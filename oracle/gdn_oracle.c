@@ -12,9 +12,9 @@
  *   1. conv      fused [q|k|v] depthwise causal conv1d over the last K raw
  *                inputs, then SiLU
  *                (pegainfer PR #1003 "shard linear-attention/GDR state per TP
- *                rank", PR body: "2D row stitch for the fused qkv [q|k|v]
- *                segments, 1D element stitch for conv1d channels";
- *                cortex commit 95dc874 "TP-aware Qwen3-Next", Architecture
+ *                rank", PR body, weight_loader bullet: the fused qkv weight
+ *                has q, k and v segments and conv1d has one weight per
+ *                channel; cortex commit 95dc874 "TP-aware Qwen3-Next", Architecture
  *                pieces, TpQwen3_5GatedDeltaNet: in_proj_qkv and conv1d.weight
  *                are fused tensors with three regions [key|key|value]).
  *   2. split     channel order [q (Hk*dk) | k (Hk*dk) | v (Hv*dv)], head-major
@@ -28,15 +28,15 @@
  *   5. recurrence, per V-head, with the post-update state used for the output:
  *                S_t = e^{g_t} S_{t-1} + beta_t k_t (v_t - e^{g_t} S_{t-1}^T k_t)^T
  *                o_t = S_t^T q_t
- *                (the "delta-rule loop" of cortex commit 95dc874,
+ *                (the per-V-head delta-rule state of cortex commit 95dc874,
  *                TpQwen3_5GatedDeltaNet bullet; the GDR recurrence as defined
  *                in Yang, Kautz & Hatamizadeh, "Gated Delta Networks: Improving
  *                Mamba2 with Delta Rule", ICLR 2025, eq. for S_t).
  *   6. gated RMSNorm   y = w * o / sqrt(mean(o^2) + eps) * SiLU(z), w shared by
- *                all V-heads (pegainfer PR #1003, PR body: "gated RMSNorm at
- *                local v heads", "norm_weight kept replicated (head-shared)";
- *                cortex commit 95dc874, "Reuses unchanged": the gated
- *                Qwen3_5RmsNormGated tail).
+ *                all V-heads (pegainfer PR #1003, PR body, batch_decode and
+ *                weights bullets: the gated norm runs per local V-head with
+ *                one replicated weight; cortex commit 95dc874, "Reuses
+ *                unchanged": the gated Qwen3_5RmsNormGated tail).
  *
  * Readings taken where the pages are silent: no conv bias; the conv weight tap
  * K-1 multiplies the current token; the conv window holds the last K raw
