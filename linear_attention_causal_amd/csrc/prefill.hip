@@ -148,26 +148,41 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int n) {
   return s;
 }
 
-// Raw (pre-conv) input of channel ch at position rel relative to the start of
-// the sequence; negative positions come from the slot's conv window (whose
-// last column is position -1) or are zero for a fresh sequence; `valid`
-// false gives zero.  Branch-free: the address is always a readable element
-// (the load is unconditional and the value is selected afterwards), so that
-// a conditional load never forces a wait on every outstanding load.
+// Raw (pre-conv) input of one channel at position `pos` relative to the
+// start of a sequence: x rows for pos >= 0, the slot's conv window (whose
+// last column is position -1) for negative pos, zero for a fresh sequence,
+// past the end, or when `valid` is false.  The two base addresses are
+// computed once per channel; a read is one select, one clamped index and one
+// unconditional load (the value is selected afterwards), so that no
+// conditional load forces a wait on every outstanding load.
 template <typename Act, int K>
-__device__ __forceinline__ float raw_input(const PrefillParams& p, const SeqInfo& si,
-                                           long long rel, int ch, bool valid = true) {
-  using io = act_io<Act>;
-  const bool in_x = rel >= 0;
-  const bool use = valid && (in_x ? rel < si.len : (si.init && rel >= -K));
-  const void* win = static_cast<const char*>(p.conv) + (size_t)si.slot * K * p.C * io::bytes;
-  const void* base = (use && in_x) ? p.x : win;
-  const size_t idx = !use ? (size_t)ch
-                   : in_x ? (size_t)(si.begin + rel) * p.C + ch
-                          : (size_t)(K + rel) * p.C + ch;
-  const float v = io::load(base, idx);
-  return use ? v : 0.f;
-}
+struct ChanReader {
+  const char* xb;      // &x[begin][ch]
+  const char* wb;      // &window[K][ch]: wb + pos * stride hits window row K + pos
+  long long stride;    // bytes between consecutive positions (C elements)
+  int len;
+  bool init;
+
+  __device__ __forceinline__ ChanReader(const PrefillParams& p, const SeqInfo& si, int ch) {
+    using io = act_io<Act>;
+    stride = (long long)p.C * io::bytes;
+    xb = static_cast<const char*>(p.x) + ((long long)si.begin * p.C + ch) * io::bytes;
+    wb = static_cast<const char*>(p.conv) + (size_t)si.slot * K * p.C * io::bytes +
+         (long long)K * stride + (long long)ch * io::bytes;
+    len = si.len;
+    init = si.init;
+  }
+
+  __device__ __forceinline__ float operator()(int pos, bool valid = true) const {
+    using io = act_io<Act>;
+    const bool in_x = pos >= 0;
+    const bool use = valid && (in_x ? pos < len : (init && pos >= -K));
+    const int pc = use ? pos : (in_x ? 0 : -1);   // a readable position either way
+    const char* a = (in_x ? xb : wb) + (long long)pc * stride;
+    const float v = io::load(a, 0);
+    return use ? v : 0.f;
+  }
+};
 
 // Causal conv + SiLU of one channel over tokens t0 .. t0+nc-1 of a sequence;
 // out[i * ld] for i < kL (rows >= nc get zero).  All kL + K - 1 inputs are
@@ -180,8 +195,9 @@ __device__ __forceinline__ void conv_channel(const PrefillParams& p, const SeqIn
 #pragma unroll
   for (int j = 0; j < K; ++j) wt[j] = io::load(p.conv_w, (size_t)ch * K + j);
   float xs[kL + K - 1];  // positions t0-(K-1) .. t0+kL-1
+  const ChanReader<Act, K> rd(p, si, ch);
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) xs[j] = raw_input<Act, K>(p, si, (long long)t0 - (K - 1) + j, ch);
+  for (int j = 0; j < K - 1; ++j) xs[j] = rd(t0 - (K - 1) + j);
   const size_t base = (size_t)(si.begin + t0) * p.C + ch;
 #pragma unroll
   for (int i = 0; i < kL; ++i) {  // clamped address, then select: no branch per load
@@ -498,16 +514,21 @@ __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// Operands of one chunk held in registers by one wave: the A fragments of
-// its token-row block (k_hat, q_hat, Tm, P) and of its two state blocks
-// (k_hat^T), plus the raw v inputs of its four token rows.
-template <int NKS, int SPW, int K>
+// Wave roles in the state kernel (8 waves; token-row block orb = wave % 4):
+//   waves 0-3  X = K S, R = beta (V - e^gamma X), V' = Tm R   (load k_hat, Tm)
+//   waves 4-7  Y = Q S, O = e^gamma Y + P V'                  (load q_hat, P)
+//   wave w < D/16 also owns state row block w (both column blocks) and
+//   loads that block's k_hat^T rows.
+// so every operand fragment of a chunk is fetched once per workgroup.
+// Operands of one chunk held in registers by one wave; the next chunk's
+// are fetched into the same registers right after their last use.
+template <int NKS, int K>
 struct ChunkOps {
-  bf16x8 kq[NKS][4];     // k_hat hi, lo, q_hat hi, lo
-  bf16x8 tp[2][4];       // Tm hi, lo, P hi, lo
-  bf16x8 kt[SPW][2][2];  // [state block][k-step][hi, lo] of k_hat^T
-  float vraw[K + 3];
-  float gam, beta;     // lane < 64: this chunk's row `lane`
+  bf16x8 fr[NKS][2];   // k_hat (waves 0-3) or q_hat (waves 4-7): hi, lo
+  bf16x8 tp[2][2];     // Tm (waves 0-3) or P (waves 4-7): [k-step][hi, lo]
+  bf16x8 kt[2][2];     // k_hat^T rows of the owned state row block
+  float vraw[2][K + 3];
+  float gam, beta;     // row `lane` of the chunk
   float glast;
 };
 
@@ -516,14 +537,14 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int NCB = DVT / 16;        // 16-wide column blocks of the tile
   constexpr int NKS = D / 32;          // k-steps over dk
-  constexpr int NST = (D / 16) * NCB;  // 16 x 16 blocks of the state tile
-  constexpr int SPW = (NST + kSW - 1) / kSW;  // ... per wave (at most)
+  constexpr int NRB = D / 16;          // 16-row blocks of the state tile
   constexpr int LS = D + 8;            // row length of the transposed state [j][d]
   constexpr int LR = kL + 8;           // row length of [j][token] tiles
-  static_assert(NCB * (kL / 16) == kSW, "one 16 x 16 output block per wave");
+  static_assert(NCB == 2 && NRB <= kSW, "tiling");
   __shared__ __attribute__((aligned(16))) __bf16 sS[2][DVT * LS];   // state, B operand
-  __shared__ __attribute__((aligned(16))) __bf16 sR[2][DVT * LR];   // R, later e^{..} V'
+  __shared__ __attribute__((aligned(16))) __bf16 sR[2][DVT * LR];   // R
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][DVT * LR];   // V'
+  __shared__ __attribute__((aligned(16))) __bf16 sD[2][DVT * LR];   // e^{gamma_L - gamma} V'
   __shared__ float sEg[kL], sBeta[kL], sDec[kL];
 
   const int n = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * DVT;
@@ -532,88 +553,89 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   const int m = h / p.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const int orb = wave & 3, ocb = wave >> 2;   // this wave's output block
+  const bool roleA = wave < 4;
+  const int orb = wave & 3;                    // token-row block
+  const bool ownsS = wave < NRB;               // state row block `wave`
   const int i0 = 16 * orb + 4 * lk;            // first of this lane's four token rows
-  const int vch = 2 * p.Hk * D + h * D + col0 + 16 * ocb + li;  // its v channel
+  const int vch0 = 2 * p.Hk * D + h * D + col0 + li;   // v channel of column block 0
   float* Sg = p.rec + ((size_t)si.slot * p.Hv + h) * D * D;
   const size_t cbase = si.len > 0 ? (size_t)p.s.chunk_base[n] : 0;
   const int nchunks = (si.len + kL - 1) / kL;
 
-  float wt[K];
+  float wt[NCB][K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) wt[k] = io::load(p.conv_w, (size_t)vch * K + k);
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int k = 0; k < K; ++k) wt[cb][k] = io::load(p.conv_w, (size_t)(vch0 + 16 * cb) * K + k);
 
-  // state blocks owned by this wave, in accumulator layout
-  // (a wave owns state block st = wave + 8q when st < NST; uniform per wave)
-  auto owns = [&](int q) { return NST % kSW == 0 || wave + kSW * q < NST; };
-  f32x4 S[SPW];
+  f32x4 S[NCB];
 #pragma unroll
-  for (int q = 0; q < SPW; ++q) {
-    S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!owns(q)) continue;
-    const int st = wave + kSW * q, rb = st / NCB, cb = st - rb * NCB;
+  for (int cb = 0; cb < NCB; ++cb) {
+    S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ownsS)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li];
-      S[q][e] = si.init ? v : 0.f;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const float v = Sg[(size_t)(16 * wave + 4 * lk + e) * D + col0 + 16 * cb + li];
+        S[cb][e] = si.init ? v : 0.f;
+      }
   }
 
-  // Loads are unconditional (the chunk index is clamped), so that the
-  // prefetch of chunk c+1 never introduces a branch and its wait.
-  auto load_kq = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+  // Loads are unconditional within a wave's role (chunk index clamped), so
+  // the prefetch of chunk c+1 never introduces a branch and its wait.
+  auto load_fr = [&](ChunkOps<NKS, K>& o, int c) {
     const size_t gk = (cbase + c) * p.Hk + m;
     const size_t ro = (gk * kL + 16 * orb + li) * D + 8 * lk;
+    const __bf16* hi = roleA ? p.s.kh[0] : p.s.qh[0];
+    const __bf16* lo = roleA ? p.s.kh[1] : p.s.qh[1];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      o.kq[ks][0] = ld8(p.s.kh[0] + ro + 32 * ks);
-      o.kq[ks][1] = ld8(p.s.kh[1] + ro + 32 * ks);
-      o.kq[ks][2] = ld8(p.s.qh[0] + ro + 32 * ks);
-      o.kq[ks][3] = ld8(p.s.qh[1] + ro + 32 * ks);
+      o.fr[ks][0] = ld8(hi + ro + 32 * ks);
+      o.fr[ks][1] = ld8(lo + ro + 32 * ks);
     }
   };
-  auto load_tp = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+  auto load_tp = [&](ChunkOps<NKS, K>& o, int c) {
     const size_t gh = (cbase + c) * p.Hv + h;
     const size_t ro = (gh * kL + 16 * orb + li) * kL + 8 * lk;
+    const __bf16* hi = roleA ? p.s.tm[0] : p.s.pm[0];
+    const __bf16* lo = roleA ? p.s.tm[1] : p.s.pm[1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      o.tp[ks][0] = ld8(p.s.tm[0] + ro + 32 * ks);
-      o.tp[ks][1] = ld8(p.s.tm[1] + ro + 32 * ks);
-      o.tp[ks][2] = ld8(p.s.pm[0] + ro + 32 * ks);
-      o.tp[ks][3] = ld8(p.s.pm[1] + ro + 32 * ks);
+      o.tp[ks][0] = ld8(hi + ro + 32 * ks);
+      o.tp[ks][1] = ld8(lo + ro + 32 * ks);
     }
   };
-  auto load_kt = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+  auto load_kt = [&](ChunkOps<NKS, K>& o, int c) {
     const size_t gk = (cbase + c) * p.Hk + m;
+    const size_t ro = (gk * D + 16 * (ownsS ? wave : 0) + li) * kL + 8 * lk;
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-      const int rb = owns(q) ? (wave + kSW * q) / NCB : 0;
-      const size_t ro = (gk * D + 16 * rb + li) * kL + 8 * lk;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        o.kt[q][ks][0] = ld8(p.s.kt[0] + ro + 32 * ks);
-        o.kt[q][ks][1] = ld8(p.s.kt[1] + ro + 32 * ks);
-      }
+    for (int ks = 0; ks < 2; ++ks) {
+      o.kt[ks][0] = ld8(p.s.kt[0] + ro + 32 * ks);
+      o.kt[ks][1] = ld8(p.s.kt[1] + ro + 32 * ks);
     }
   };
-  auto load_misc = [&](ChunkOps<NKS, SPW, K>& o, int c) {
+  const ChanReader<Act, K> vrd[NCB] = {ChanReader<Act, K>(p, si, vch0),
+                                       ChanReader<Act, K>(p, si, vch0 + 16)};
+  auto load_misc = [&](ChunkOps<NKS, K>& o, int c) {
     const int t0 = c * kL, nc = min(kL, si.len - t0);
     const size_t gh = (cbase + c) * p.Hv + h;
     o.glast = p.s.gam[gh * kL + nc - 1];
     o.gam = p.s.gam[gh * kL + lane];
     o.beta = p.s.beta[gh * kL + lane];
+    if (roleA)
 #pragma unroll
-    for (int k = 0; k < K + 3; ++k) {
-      const int pos = t0 + i0 - (K - 1) + k;  // relative to the sequence start
-      o.vraw[k] = raw_input<Act, K>(p, si, pos, vch, pos < t0 + nc);
-    }
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int k = 0; k < K + 3; ++k) {
+          const int pos = t0 + i0 - (K - 1) + k;  // relative to the sequence start
+          o.vraw[cb][k] = vrd[cb](pos, pos < t0 + nc);
+        }
   };
 
-  ChunkOps<NKS, SPW, K> ops;
+  ChunkOps<NKS, K> ops;
   if (nchunks > 0) {
-    load_kq(ops, 0);
+    load_fr(ops, 0);
     load_tp(ops, 0);
-    load_kt(ops, 0);
+    if (ownsS) load_kt(ops, 0);
     load_misc(ops, 0);
   }
   for (int c = 0; c < nchunks; ++c) {
@@ -628,117 +650,136 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       sDec[tid] = ok ? __expf(ops.glast - ops.gam) : 0.f;
     }
     const float egl = __expf(ops.glast);
-    float v4[4];
+    float v4[NCB][4];
+    if (roleA)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float acc = 0.f;
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int k = 0; k < K; ++k) acc = fmaf(wt[k], ops.vraw[e + k], acc);
-      v4[e] = i0 + e < nc ? silu_fast(acc) : 0.f;
-    }
+        for (int e = 0; e < 4; ++e) {
+          float acc = 0.f;
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-      if (!owns(q)) continue;
-      const int st = wave + kSW * q, rb = st / NCB, cb = st - rb * NCB;
+          for (int k = 0; k < K; ++k) acc = fmaf(wt[cb][k], ops.vraw[cb][e + k], acc);
+          v4[cb][e] = i0 + e < nc ? silu_fast(acc) : 0.f;
+        }
+    if (ownsS)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        __bf16 hi, lo;
-        split_bf16(S[q][e], hi, lo);
-        const int idx = (16 * cb + li) * LS + 16 * rb + 4 * lk + e;
-        sS[0][idx] = hi;
-        sS[1][idx] = lo;
-      }
-    }
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 hi, lo;
+          split_bf16(S[cb][e], hi, lo);
+          const int idx = (16 * cb + li) * LS + 16 * wave + 4 * lk + e;
+          sS[0][idx] = hi;
+          sS[1][idx] = lo;
+        }
     __syncthreads();
-
-    // X = K S and Y = Q S for this wave's output block
-    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int bo = (16 * ocb + li) * LS + 32 * ks + 8 * lk;
-      const bf16x8 sh = ld8(&sS[0][bo]), sl = ld8(&sS[1][bo]);
-      X = mfma3(ops.kq[ks][0], ops.kq[ks][1], sh, sl, X);
-      Y = mfma3(ops.kq[ks][2], ops.kq[ks][3], sh, sl, Y);
-    }
-    load_kq(ops, cn);
-    // R = beta (V - e^gamma X) -> LDS;  O = e^gamma Y (inter-chunk part)
-    f32x4 O;
-    {
-      const int j = 16 * ocb + li;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        const float r = sBeta[i] * (v4[e] - sEg[i] * X[e]);
-        O[e] = sEg[i] * Y[e];
-        __bf16 hi, lo;
-        split_bf16(r, hi, lo);
-        sR[0][j * LR + i] = hi;
-        sR[1][j * LR + i] = lo;
-      }
-    }
-    const float gl_cur = ops.glast;
-    (void)gl_cur;
     load_misc(ops, cn);
-    __syncthreads();
-    // V' = Tm R for this wave's output block
-    f32x4 Vp = {0.f, 0.f, 0.f, 0.f};
+
+    // X = K S (waves 0-3) or Y = Q S (waves 4-7) for token-row block orb
+    f32x4 XY[NCB];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int bo = (16 * ocb + li) * LR + 32 * ks + 8 * lk;
-      Vp = mfma3(ops.tp[ks][0], ops.tp[ks][1], ld8(&sR[0][bo]), ld8(&sR[1][bo]), Vp);
+    for (int cb = 0; cb < NCB; ++cb) XY[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
+        XY[cb] = mfma3(ops.fr[ks][0], ops.fr[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]), XY[cb]);
+      }
+    load_fr(ops, cn);
+    f32x4 O[NCB];
+    if (roleA) {
+      // R = beta (V - e^gamma X) -> LDS
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int j = 16 * cb + li;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          const float r = sBeta[i] * (v4[cb][e] - sEg[i] * XY[cb][e]);
+          __bf16 hi, lo;
+          split_bf16(r, hi, lo);
+          sR[0][j * LR + i] = hi;
+          sR[1][j * LR + i] = lo;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[cb][e] = sEg[i0 + e] * XY[cb][e];
     }
-    __syncthreads();  // every wave is done reading R
-    {
-      const int j = 16 * ocb + li;
+    __syncthreads();
+    if (roleA) {
+      // V' = Tm R -> LDS, plain and scaled by e^{gamma_last - gamma}
+      f32x4 Vp[NCB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        __bf16 hi, lo;
-        split_bf16(Vp[e], hi, lo);
-        sV[0][j * LR + i] = hi;
-        sV[1][j * LR + i] = lo;
-        split_bf16(sDec[i] * Vp[e], hi, lo);
-        sR[0][j * LR + i] = hi;
-        sR[1][j * LR + i] = lo;
+      for (int cb = 0; cb < NCB; ++cb) Vp[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+          Vp[cb] = mfma3(ops.tp[ks][0], ops.tp[ks][1], ld8(&sR[0][bo]), ld8(&sR[1][bo]), Vp[cb]);
+        }
+      load_tp(ops, cn);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int j = 16 * cb + li;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          __bf16 hi, lo;
+          split_bf16(Vp[cb][e], hi, lo);
+          sV[0][j * LR + i] = hi;
+          sV[1][j * LR + i] = lo;
+          split_bf16(sDec[i] * Vp[cb][e], hi, lo);
+          sD[0][j * LR + i] = hi;
+          sD[1][j * LR + i] = lo;
+        }
       }
     }
     __syncthreads();
-    // O += P V'  and store the pre-norm output
+    if (!roleA) {
+      // O += P V'  and store the pre-norm output
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int bo = (16 * ocb + li) * LR + 32 * ks + 8 * lk;
-      O = mfma3(ops.tp[ks][2], ops.tp[ks][3], ld8(&sV[0][bo]), ld8(&sV[1][bo]), O);
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+          O[cb] = mfma3(ops.tp[ks][0], ops.tp[ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]), O[cb]);
+        }
+      load_tp(ops, cn);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          if (i < nc)
+            p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li] = O[cb][e];
+        }
     }
-    load_tp(ops, cn);
+    if (ownsS) {
+      // S <- e^{gamma_last} S + K^T (e^{gamma_last - gamma} V')
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = i0 + e;
-      if (i < nc)
-        p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * ocb + li] = O[e];
-    }
-    // S <- e^{gamma_last} S + K^T (e^{gamma_last - gamma} V')
+      for (int cb = 0; cb < NCB; ++cb) {
+        S[cb] *= egl;
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-      if (!owns(q)) continue;
-      const int cb = (wave + kSW * q) % NCB;
-      S[q] *= egl;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-        S[q] = mfma3(ops.kt[q][ks][0], ops.kt[q][ks][1], ld8(&sR[0][bo]), ld8(&sR[1][bo]), S[q]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+          S[cb] = mfma3(ops.kt[ks][0], ops.kt[ks][1], ld8(&sD[0][bo]), ld8(&sD[1][bo]), S[cb]);
+        }
       }
+      load_kt(ops, cn);
     }
-    load_kt(ops, cn);
   }
 
+  if (ownsS)
 #pragma unroll
-  for (int q = 0; q < SPW; ++q) {
-    if (!owns(q)) continue;
-    const int st = wave + kSW * q, rb = st / NCB, cb = st - rb * NCB;
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li] = S[q][e];
-  }
+      for (int e = 0; e < 4; ++e)
+        Sg[(size_t)(16 * wave + 4 * lk + e) * D + col0 + 16 * cb + li] = S[cb][e];
 
   // Final conv window = the last K raw inputs of [window ; tokens], for this
   // tile's v channels, plus the q/k channels of K-head m from tile 0 of its
@@ -754,9 +795,10 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       const int ch = e < DVT ? vbase + e
                    : e < DVT + D ? m * D + (e - DVT)
                                  : (p.Hk + m) * D + (e - DVT - D);
+      const ChanReader<Act, K> rd(p, si, ch);
       float vals[K];
 #pragma unroll
-      for (int j = 0; j < K; ++j) vals[j] = raw_input<Act, K>(p, si, (long long)si.len - K + j, ch);
+      for (int j = 0; j < K; ++j) vals[j] = rd(si.len - K + j);
 #pragma unroll
       for (int j = 0; j < K; ++j) io::store(win, (size_t)j * p.C + ch, vals[j]);
     }
