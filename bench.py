@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="headline decode only (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy kernel (the reference "
+                         "for scaling the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -161,17 +164,65 @@ def bench_decode(args):
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / R
     per_launch = step_bytes(geom, B, 2)
     achieved = per_launch / (launch_ms * 1e-3)
+    rec = recorded_traffic()
     return dict(
         tokens_per_s=B * nsteps / dt, ms_per_step=dt * 1e3 / nsteps, steps=nsteps, B=B,
         workload=work.name, geom=geom,
         eager={"tokens_per_s": B * args.steps / eager_dt,
                "ms_per_step": eager_dt * 1e3 / args.steps},
         roofline={"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
-                  "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
+                  "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                  "traffic": rec["hbm_bytes_per_launch"] if rec else None,
+                  "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
                   "kernel": "gdn::decode_step_kernel<__bf16, 128, 2, 4>",
                   "bytes_per_launch": per_launch, "mean_launch_us": launch_ms * 1e3,
                   "timing": "HIP events around graph replays of 16 back-to-back launches"},
         step_hbm_frac=per_launch / (dt / nsteps) / HBM_PEAK)
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_step_b16_hk8_hv16_d128_traffic.md")
+TRAFFIC_SOURCES = ("linear_attention_causal_amd/csrc/decode.hip",
+                   "linear_attention_causal_amd/csrc/gdn_device.hpp")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter record (FETCH_SIZE
+    and WRITE_SIZE passes, each scaled by the same counter's reading on a plain
+    copy of known size), or None when there is no record or the kernel source
+    has changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            text = f.read()
+    except OSError:
+        return None
+    rec = None
+    for ln in text.splitlines():
+        if ln.startswith("record: "):
+            rec = json.loads(ln[len("record: "):])
+    if not rec or rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec
+
+
+def calibration_copy(nbytes=512 << 20, reps=4):
+    """A plain elementwise copy (read nbytes, write nbytes) run a few times; its
+    counter readings calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {nbytes} bytes read + {nbytes} written per launch, {reps} launches")
 
 
 # ------------------------------------------------------------------ prefill
@@ -363,6 +414,8 @@ def main():
     torch.cuda.set_device(0)
     log("[bench] decode headline")
     dec = bench_decode(args)
+    if args.calibration_copy:
+        calibration_copy()
     line = {
         "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": dec["steps"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],

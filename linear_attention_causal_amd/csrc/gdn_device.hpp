@@ -30,6 +30,12 @@ template <> struct act_io<float> {
   static __device__ __forceinline__ void store4(void* p, size_t i, f32x4 v) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = v;
   }
+  // Unconverted element, for loads whose conversion is deferred to the use.
+  using raw_t = float;
+  static __device__ __forceinline__ raw_t load_raw(const void* p, size_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ float from_raw(raw_t r) { return r; }
   static constexpr int bytes = 4;
 };
 
@@ -65,6 +71,11 @@ template <> struct act_io<__bf16> {
     u.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
     *reinterpret_cast<uint2*>(static_cast<unsigned short*>(p) + i) = u;
   }
+  using raw_t = uint32_t;   // zero-extended bits
+  static __device__ __forceinline__ raw_t load_raw(const void* p, size_t i) {
+    return static_cast<const unsigned short*>(p)[i];
+  }
+  static __device__ __forceinline__ float from_raw(raw_t r) { return bf16_bits_to_f32(r); }
   static constexpr int bytes = 2;
 };
 

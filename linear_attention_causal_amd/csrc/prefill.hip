@@ -173,13 +173,20 @@ struct ChanReader {
     init = si.init;
   }
 
-  __device__ __forceinline__ float operator()(int pos, bool valid = true) const {
-    using io = act_io<Act>;
+  // Unconverted element at `pos` (a readable address whatever `pos` is) and
+  // whether it is part of the input; the caller applies both when it uses it,
+  // so a prefetch leaves nothing to wait for.
+  __device__ __forceinline__ typename act_io<Act>::raw_t fetch(int pos, bool valid, bool& use) const {
     const bool in_x = pos >= 0;
-    const bool use = valid && (in_x ? pos < len : (init && pos >= -K));
-    const int pc = use ? pos : (in_x ? 0 : -1);   // a readable position either way
+    use = valid & (in_x ? pos < len : (init & (pos >= -K)));
+    const int pc = use ? pos : (in_x ? 0 : -1);
     const char* a = (in_x ? xb : wb) + (long long)pc * stride;
-    const float v = io::load(a, 0);
+    return act_io<Act>::load_raw(a, 0);
+  }
+
+  __device__ __forceinline__ float operator()(int pos, bool valid = true) const {
+    bool use;
+    const float v = act_io<Act>::from_raw(fetch(pos, valid, use));
     return use ? v : 0.f;
   }
 };
@@ -522,12 +529,13 @@ __device__ __forceinline__ float silu_fast(float x) {
 // so every operand fragment of a chunk is fetched once per workgroup.
 // Operands of one chunk held in registers by one wave; the next chunk's
 // are fetched into the same registers right after their last use.
-template <int NKS, int K>
+template <typename Act, int NKS, int K>
 struct ChunkOps {
   bf16x8 fr[NKS][2];   // k_hat (waves 0-3) or q_hat (waves 4-7): hi, lo
   bf16x8 tp[2][2];     // Tm (waves 0-3) or P (waves 4-7): [k-step][hi, lo]
   bf16x8 kt[2][2];     // k_hat^T rows of the owned state row block
-  float vraw[2][K + 3];
+  typename act_io<Act>::raw_t vraw[2][K + 3];   // conv inputs, unconverted
+  uint32_t vuse;                                // bit cb*(K+3)+k: vraw[cb][k] is input
   float gam, beta;     // row `lane` of the chunk
   float glast;
 };
@@ -582,7 +590,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
 
   // Loads are unconditional within a wave's role (chunk index clamped), so
   // the prefetch of chunk c+1 never introduces a branch and its wait.
-  auto load_fr = [&](ChunkOps<NKS, K>& o, int c) {
+  auto load_fr = [&](ChunkOps<Act, NKS, K>& o, int c) {
     const size_t gk = (cbase + c) * p.Hk + m;
     const size_t ro = (gk * kL + 16 * orb + li) * D + 8 * lk;
     const __bf16* hi = roleA ? p.s.kh[0] : p.s.qh[0];
@@ -593,7 +601,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       o.fr[ks][1] = ld8(lo + ro + 32 * ks);
     }
   };
-  auto load_tp = [&](ChunkOps<NKS, K>& o, int c) {
+  auto load_tp = [&](ChunkOps<Act, NKS, K>& o, int c) {
     const size_t gh = (cbase + c) * p.Hv + h;
     const size_t ro = (gh * kL + 16 * orb + li) * kL + 8 * lk;
     const __bf16* hi = roleA ? p.s.tm[0] : p.s.pm[0];
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       o.tp[ks][1] = ld8(lo + ro + 32 * ks);
     }
   };
-  auto load_kt = [&](ChunkOps<NKS, K>& o, int c) {
+  auto load_kt = [&](ChunkOps<Act, NKS, K>& o, int c) {
     const size_t gk = (cbase + c) * p.Hk + m;
     const size_t ro = (gk * D + 16 * (ownsS ? wave : 0) + li) * kL + 8 * lk;
 #pragma unroll
@@ -615,23 +623,28 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   };
   const ChanReader<Act, K> vrd[NCB] = {ChanReader<Act, K>(p, si, vch0),
                                        ChanReader<Act, K>(p, si, vch0 + 16)};
-  auto load_misc = [&](ChunkOps<NKS, K>& o, int c) {
+  auto load_misc = [&](ChunkOps<Act, NKS, K>& o, int c) {
     const int t0 = c * kL, nc = min(kL, si.len - t0);
     const size_t gh = (cbase + c) * p.Hv + h;
     o.glast = p.s.gam[gh * kL + nc - 1];
     o.gam = p.s.gam[gh * kL + lane];
     o.beta = p.s.beta[gh * kL + lane];
-    if (roleA)
+    if (roleA) {
+      uint32_t bits = 0;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int k = 0; k < K + 3; ++k) {
           const int pos = t0 + i0 - (K - 1) + k;  // relative to the sequence start
-          o.vraw[cb][k] = vrd[cb](pos, pos < t0 + nc);
+          bool use;
+          o.vraw[cb][k] = vrd[cb].fetch(pos, pos < t0 + nc, use);
+          bits |= (uint32_t)use << (cb * (K + 3) + k);
         }
+      o.vuse = bits;
+    }
   };
 
-  ChunkOps<NKS, K> ops;
+  ChunkOps<Act, NKS, K> ops;
   if (nchunks > 0) {
     load_fr(ops, 0);
     load_tp(ops, 0);
@@ -653,14 +666,19 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
     float v4[NCB][4];
     if (roleA)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int cb = 0; cb < NCB; ++cb) {
+        float xr[K + 3];
+#pragma unroll
+        for (int k = 0; k < K + 3; ++k)
+          xr[k] = (ops.vuse >> (cb * (K + 3) + k)) & 1u ? io::from_raw(ops.vraw[cb][k]) : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float acc = 0.f;
 #pragma unroll
-          for (int k = 0; k < K; ++k) acc = fmaf(wt[cb][k], ops.vraw[cb][e + k], acc);
+          for (int k = 0; k < K; ++k) acc = fmaf(wt[cb][k], xr[e + k], acc);
           v4[cb][e] = i0 + e < nc ? silu_fast(acc) : 0.f;
         }
+      }
     if (ownsS)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
