@@ -79,6 +79,13 @@ template <> struct act_io<__bf16> {
   static constexpr int bytes = 2;
 };
 
+// Index of the calling wave in its workgroup, in a scalar register: role
+// branches and operand-pointer selects on it stay uniform (scalar) instead of
+// becoming per-lane selects that fetch kernel arguments with vector loads.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
+
 // ---------------------------------------------------------------- math
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }

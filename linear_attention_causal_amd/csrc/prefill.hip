@@ -3,31 +3,33 @@
 // batch_decode/prefill bullet, and Description, GdrChunkwiseScratch35).
 //
 // Blocked form of the gated delta rule over chunks of L = 64 tokens that
-// never span two sequences.  Inside a chunk, with gamma_i the running sum of
-// the gates g and beta_i the write strengths (both per V-head),
+// never span two sequences (the WY representation of the chunk, Gated
+// DeltaNet paper, chunkwise training section).  Inside a chunk, with gamma_i
+// the running sum of the gates g and beta_i the write strengths (both per
+// V-head),
 //   A   = strict_lower(beta_i e^{gamma_i - gamma_j} k_i . k_j)
 //   Tm  = (I + A)^{-1}                                  (unit lower triangular)
-//   V'  = Tm diag(beta) (V - diag(e^gamma) K S)         (the writes u_t)
+//   W   = Tm diag(beta e^gamma) K,   U = Tm diag(beta) V
+//   V'  = U - W S                                        (the writes u_t)
 //   O   = diag(e^gamma) Q S + P V',   P = mask_{j<=i}(e^{gamma_i-gamma_j}) * (Q K^T)
 //   S  <- e^{gamma_last} S + K^T diag(e^{gamma_last-gamma}) V'
 // which is the token recurrence S_t = e^{g_t}S_{t-1} + beta_t k_t (v_t -
-// e^{g_t} S_{t-1}^T k_t)^T, o_t = S_t^T q_t unrolled over the chunk (the
-// usual WY/UT form with W = Tm diag(beta e^gamma) K never formed: Tm is
-// applied to the small chunk x dv right-hand side instead).  Decays are only
-// formed as e^{gamma_i - gamma_j} with j <= i (<= 1).
+// e^{g_t} S_{t-1}^T k_t)^T, o_t = S_t^T q_t unrolled over the chunk.  Decays
+// are only formed as e^{gamma_i - gamma_j} with j <= i (<= 1).
 //
 // Launches, in stream order:
 //   0. plan   one workgroup: chunk_base[n] = number of chunks before sequence n.
 //   1. prep   (chunk, sequence, K-head), all chunks in parallel: conv + SiLU
-//             of q/k, l2norm, K K^T and Q K^T once per K-head; per V-head the
-//             gates, their running sum, Tm (blocked 16 x 16 triangular
-//             inverse) and P.  Operands are written as bf16 (hi, lo) pairs in
-//             the exact fragment layout of the next kernel.
-//   2. state  (sequence, V-head, dv tile), sequential over the chunks of a
-//             sequence, the dv columns of S split over workgroups (they
-//             evolve independently): K S, Q S, V', P V' and the state carry,
-//             on 3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo + lo*hi with f32
-//             accumulation, about 2^-16 relative), then O (pre-norm) to f32.
+//             of q/k/v, l2norm, K K^T and Q K^T once per K-head; per V-head
+//             the gates, their running sum, Tm (blocked 16 x 16 triangular
+//             inverse), P, W and U.  Operands are written as bf16 (hi, lo)
+//             pairs (U as f32) in the fragment layout of the next kernel.
+//   2. state  (sequence, V-head, 16 dv columns), sequential over the chunks
+//             of a sequence, the dv columns of S split over workgroups (they
+//             evolve independently): V' = U - W S and the state carry on one
+//             half of the waves, O = e^gamma Q S + P V' on the other half, on
+//             3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo + lo*hi with f32
+//             accumulation, about 2^-16 relative), O (pre-norm) to f32.
 //   3. norm   (chunk, sequence, V-head): gated RMSNorm with SiLU(z) -> y.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -43,41 +45,44 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Chunk-indexed scratch: chunk g = chunk_base[n] + c holds 64 rows (rows past
-// the end of a sequence are written as zeros by the prep kernel).
+// the end of a sequence are written as zeros by the prep kernel).  Everything
+// the sequential state kernel reads is stored fragment-major (see frag_at):
+// one wave's MFMA operand tile is one contiguous 1 KB block.
 struct PrefillScratch {
   int32_t* chunk_base;     // [N+1]
-  __bf16* qh[2];           // hi, lo: [G][Hk][64][D]   q_hat rows
-  __bf16* kh[2];           //         [G][Hk][64][D]   k_hat rows
-  __bf16* kt[2];           //         [G][Hk][D][64]   k_hat transposed
-  __bf16* tm[2];           //         [G][Hv][64][64]  (I + A)^{-1}
-  __bf16* pm[2];           //         [G][Hv][64][64]  masked, decayed Q K^T
+  __bf16* qh[2];           // hi, lo: [G][Hk] 64 x D    q_hat, A-operand blocks
+  __bf16* kt[2];           //         [G][Hk] D x 64    k_hat^T, A-operand blocks
+  __bf16* w[2];            //         [G][Hv] 64 x D    -Tm diag(beta e^gamma) K
+  __bf16* pm[2];           //         [G][Hv] 64 x 64   masked, decayed Q K^T
+  float* ut;               // [G][Hv] 64 x D Tm diag(beta) V, accumulator blocks
   float* gam;              // [G][Hv][64] running sum of g
-  float* beta;             // [G][Hv][64]
   float* o;                // [T][Hv][D] pre-norm output
 };
 
 static size_t chunk_bound(long long T, long long N) { return (size_t)((T + kL - 1) / kL + N); }
 
+constexpr int kScratchParts = 12;
+
 struct ScratchPlan {
-  size_t off[14];
+  size_t off[kScratchParts];
   size_t total;
 };
 
 static ScratchPlan plan_scratch(const gdn_geometry& g, long long T, long long N) {
   const size_t G = chunk_bound(T, N), D = (size_t)g.head_k_dim;
   const size_t Hk = (size_t)g.num_k_heads, Hv = (size_t)g.num_v_heads;
-  const size_t sizes[14] = {
+  const size_t sizes[kScratchParts] = {
       (size_t)(N + 1) * 4,
       G * Hk * kL * D * 2, G * Hk * kL * D * 2,      // qh
-      G * Hk * kL * D * 2, G * Hk * kL * D * 2,      // kh
       G * Hk * D * kL * 2, G * Hk * D * kL * 2,      // kt
-      G * Hv * kL * kL * 2, G * Hv * kL * kL * 2,    // tm
+      G * Hv * kL * D * 2, G * Hv * kL * D * 2,      // w
       G * Hv * kL * kL * 2, G * Hv * kL * kL * 2,    // pm
-      G * Hv * kL * 4, G * Hv * kL * 4,              // gam, beta
+      G * Hv * D * kL * 4,                           // ut
+      G * Hv * kL * 4,                               // gam
       (size_t)T * Hv * D * 4};                       // o
   ScratchPlan sp;
   size_t at = 0;
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < kScratchParts; ++i) {
     sp.off[i] = at;
     at += align256(sizes[i]);
   }
@@ -96,14 +101,13 @@ static PrefillScratch carve(const gdn_geometry& g, long long T, long long N, voi
   s.chunk_base = reinterpret_cast<int32_t*>(c + sp.off[0]);
   for (int k = 0; k < 2; ++k) {
     s.qh[k] = reinterpret_cast<__bf16*>(c + sp.off[1 + k]);
-    s.kh[k] = reinterpret_cast<__bf16*>(c + sp.off[3 + k]);
-    s.kt[k] = reinterpret_cast<__bf16*>(c + sp.off[5 + k]);
-    s.tm[k] = reinterpret_cast<__bf16*>(c + sp.off[7 + k]);
-    s.pm[k] = reinterpret_cast<__bf16*>(c + sp.off[9 + k]);
+    s.kt[k] = reinterpret_cast<__bf16*>(c + sp.off[3 + k]);
+    s.w[k] = reinterpret_cast<__bf16*>(c + sp.off[5 + k]);
+    s.pm[k] = reinterpret_cast<__bf16*>(c + sp.off[7 + k]);
   }
-  s.gam = reinterpret_cast<float*>(c + sp.off[11]);
-  s.beta = reinterpret_cast<float*>(c + sp.off[12]);
-  s.o = reinterpret_cast<float*>(c + sp.off[13]);
+  s.ut = reinterpret_cast<float*>(c + sp.off[9]);
+  s.gam = reinterpret_cast<float*>(c + sp.off[10]);
+  s.o = reinterpret_cast<float*>(c + sp.off[11]);
   return s;
 }
 
@@ -233,12 +237,24 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// c += (ah + al)(bh + bl), dropping the al*bl term (small terms first).
-__device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
-  c = mfma_bf16(al, bh, c);
-  c = mfma_bf16(ah, bl, c);
-  return mfma_bf16(ah, bh, c);
+// (ah + al)(bh + bl) without the al*bl term, as three independent products
+// accumulated separately so that consecutive k-steps of one tile do not wait
+// on each other's passes; fold() adds the small terms first.
+struct Acc3 {
+  f32x4 hh, lh, hl;
+};
+
+__device__ __forceinline__ Acc3 acc3(f32x4 init) {
+  return Acc3{init, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 }
+
+__device__ __forceinline__ void mfma3(Acc3& c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+  c.hh = mfma_bf16(ah, bh, c.hh);
+  c.lh = mfma_bf16(al, bh, c.lh);
+  c.hl = mfma_bf16(ah, bl, c.hl);
+}
+
+__device__ __forceinline__ f32x4 fold(const Acc3& c) { return (c.lh + c.hl) + c.hh; }
 
 __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
   hi = static_cast<__bf16>(v);
@@ -260,6 +276,37 @@ __device__ __forceinline__ bf16x8 ld8(const __bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Fragment-major storage of an R x Kd bf16 MFMA A operand (R, Kd multiples
+// of 16 and 32): tile (row block rb, k-step ks) is block rb * (Kd / 32) + ks
+// of 64 lanes x 8 elements, lane li + 16 lk holding row 16 rb + li, columns
+// 32 ks + 8 lk .. +7.  Element offset of (row, col), col a multiple of 4:
+__device__ __forceinline__ size_t frag_at(size_t mat, int rows, int kd, int row, int col) {
+  const size_t blk = mat * (size_t)((rows >> 4) * (kd >> 5)) + (row >> 4) * (kd >> 5) + (col >> 5);
+  const int ln = (row & 15) + 16 * ((col & 31) >> 3);
+  return (blk * 64 + ln) * 8 + (col & 7);
+}
+
+// Element offset of lane `lane` in block `blk` of a fragment-major operand.
+__device__ __forceinline__ size_t frag_lane(size_t blk, int lane) {
+  return (blk * 64 + lane) * 8;
+}
+
+// Four f32 split into bf16 (hi, lo) and stored as two 8-byte packs.
+__device__ __forceinline__ void store_split4(__bf16* hi, __bf16* lo, f32x4 v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __bf16 a, b;
+    split_bf16(v[e], a, b);
+    h[e] = a;
+    l[e] = b;
+  }
+  *reinterpret_cast<bf16x4*>(hi) = h;
+  *reinterpret_cast<bf16x4*>(lo) = l;
+}
+
 // ------------------------------------------------------------------ 0. plan
 
 // chunk_base[n] = sum over n' < n of ceil(len(n') / 64), chunk_base[N] = total.
@@ -274,7 +321,7 @@ __device__ __forceinline__ int seq_chunks(const int32_t* cu, int n, long long T)
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t* cu, int N, long long T,
                                                             int32_t* chunk_base) {
   __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int per = (N + 1023) / 1024;
   const int n0 = tid * per, n1 = min(N, n0 + per);
   int local = 0;
@@ -322,7 +369,7 @@ __device__ __forceinline__ f32x4 mm16(const float* A, int lda, const float* B, i
 // Called by all four waves; ends with the result in sT.
 template <int LDL>
 __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
   // strictly upper blocks are zero
   for (int idx = tid; idx < kL * kL; idx += kNT) {
@@ -366,19 +413,30 @@ __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int ti
   }
 }
 
+// One workgroup per (chunk, sequence, K-head).  Everything here depends on
+// the chunk's own tokens only (WY form of the chunk, Gated DeltaNet paper,
+// chunkwise training section):
+//   q_hat, k_hat^T                          per K-head, as bf16 hi/lo rows
+//   gamma = running sum of g, beta          per V-head
+//   A = strict_lower(beta_i e^{gamma_i - gamma_j} k_i.k_j), Tm = (I + A)^{-1}
+//   P = lower(e^{gamma_i - gamma_j} q_i.k_j)
+//   W = Tm diag(beta e^gamma) K,  U = Tm diag(beta) V
+// so that the sequential pass only has V' = U - W S and the state update left.
 template <typename Act, int D, int K>
 __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   using io = act_io<Act>;
-  constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NKS = D / 32;
-  constexpr int TILE = kL * (LDD > LDL ? LDD : LDL);
-  __shared__ __attribute__((aligned(16))) float sQ[TILE];   // q_hat; later A
-  __shared__ __attribute__((aligned(16))) float sK[TILE];   // k_hat; later Tm
+  constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NKS = D / 32, NDB = D / 16;
+  constexpr int LDH = kL + 8;   // bf16 row length of the split Tm
+  constexpr int R1A = kL * LDD, R1B = 2 * kL * LDL, R1C = D * LDL;
+  constexpr int R1 = R1A > R1B ? (R1A > R1C ? R1A : R1C) : (R1B > R1C ? R1B : R1C);
+  static_assert(kNW * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the Tm tiles");
+  __shared__ __attribute__((aligned(16))) float sR1[R1];        // q_hat; then A | Tm; then v^T
+  __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k_hat rows
   __shared__ float sG[kL * LDL];                                // K K^T
   __shared__ float sQK[kL * LDL];                               // Q K^T
-  __shared__ float sM[kNW * 16 * 17];
-  __shared__ float sGam[kL], sBeta[kL];
-  float* sA = sQ;
-  float* sT = sK;
+  __shared__ __attribute__((aligned(16))) __bf16 sTm[2][kL * LDH];   // Tm hi, lo
+  __shared__ float sGam[kL], sBeta[kL], sSc[kL];
+  float* sQ = sR1;
 
   const int c = blockIdx.x, n = blockIdx.y, m = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
@@ -387,7 +445,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   const int nc = min(kL, si.len - t0);
   const long long tok0 = si.begin + t0;
   const size_t g = (size_t)p.s.chunk_base[n] + c;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
   // conv + SiLU of q_m and k_m
@@ -415,20 +473,17 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     }
   }
   __syncthreads();
-  // q_hat, k_hat rows and k_hat^T as bf16 (hi, lo) fragments
+  // q_hat rows and k_hat^T as bf16 (hi, lo) fragments
   {
-    const size_t rows = (g * p.Hk + m) * kL;
+    const size_t gk = g * p.Hk + m;
     for (int u = tid; u < kL * (D / 8); u += kNT) {
       const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
       bf16x8 h, l;
       split8(sQ + i * LDD + d0, h, l);
-      *reinterpret_cast<bf16x8*>(p.s.qh[0] + (rows + i) * D + d0) = h;
-      *reinterpret_cast<bf16x8*>(p.s.qh[1] + (rows + i) * D + d0) = l;
-      split8(sK + i * LDD + d0, h, l);
-      *reinterpret_cast<bf16x8*>(p.s.kh[0] + (rows + i) * D + d0) = h;
-      *reinterpret_cast<bf16x8*>(p.s.kh[1] + (rows + i) * D + d0) = l;
+      const size_t at = frag_at(gk, kL, D, i, d0);
+      *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
+      *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;
     }
-    const size_t trow = (g * p.Hk + m) * D;
     for (int u = tid; u < D * (kL / 8); u += kNT) {
       const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
       float v[8];
@@ -436,8 +491,9 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d];
       bf16x8 h, l;
       split8(v, h, l);
-      *reinterpret_cast<bf16x8*>(p.s.kt[0] + (trow + d) * kL + i0) = h;
-      *reinterpret_cast<bf16x8*>(p.s.kt[1] + (trow + d) * kL + i0) = l;
+      const size_t at = frag_at(gk, D, kL, d, i0);
+      *reinterpret_cast<bf16x8*>(p.s.kt[0] + at) = h;
+      *reinterpret_cast<bf16x8*>(p.s.kt[1] + at) = l;
     }
   }
   // K K^T and Q K^T, lower block triangle, 3-pass bf16
@@ -447,20 +503,24 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     while (rem > I) { rem -= I + 1; ++I; }
     const int J = rem;
     const float* Asrc = isG ? sK : sQ;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    Acc3 acc = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8 ah, al, bh, bl;
       split8(Asrc + (16 * I + li) * LDD + 32 * ks + 8 * lk, ah, al);
       split8(sK + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
-      acc = mfma3(ah, al, bh, bl, acc);
+      mfma3(acc, ah, al, bh, bl);
     }
+    const f32x4 r = fold(acc);
     float* dst = isG ? sG : sQK;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[(16 * I + 4 * lk + e) * LDL + 16 * J + li] = acc[e];
+    for (int e = 0; e < 4; ++e) dst[(16 * I + 4 * lk + e) * LDL + 16 * J + li] = r[e];
   }
-  __syncthreads();  // q/k tiles are free from here on (reused as A and Tm)
+  __syncthreads();  // the q tile is free from here on (reused as A, Tm, then v^T)
 
+  float* sA = sR1;
+  float* sT = sR1 + kL * LDL;
+  float* sVt = sR1;
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = m * p.r + hh;
     const size_t gh = g * p.Hv + h;
@@ -476,8 +536,8 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       }
       sGam[lane] = gv;
       sBeta[lane] = bv;
+      sSc[lane] = bv * expf(gv);
       p.s.gam[gh * kL + lane] = gv;
-      p.s.beta[gh * kL + lane] = bv;
     }
     __syncthreads();
     // A (for the inverse) and P (written out as fragments)
@@ -495,17 +555,66 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       }
       bf16x8 h8, l8;
       split8(v, h8, l8);
-      *reinterpret_cast<bf16x8*>(p.s.pm[0] + (gh * kL + i) * kL + j0) = h8;
-      *reinterpret_cast<bf16x8*>(p.s.pm[1] + (gh * kL + i) * kL + j0) = l8;
+      const size_t at = frag_at(gh, kL, kL, i, j0);
+      *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
+      *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;
     }
     __syncthreads();
-    unit_lower_inverse<LDL>(sA, sT, sM, tid);
+    unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTm[0][0]), tid);
     for (int u = tid; u < kL * (kL / 8); u += kNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
       bf16x8 h8, l8;
       split8(sT + i * LDL + j0, h8, l8);
-      *reinterpret_cast<bf16x8*>(p.s.tm[0] + (gh * kL + i) * kL + j0) = h8;
-      *reinterpret_cast<bf16x8*>(p.s.tm[1] + (gh * kL + i) * kL + j0) = l8;
+      *reinterpret_cast<bf16x8*>(&sTm[0][i * LDH + j0]) = h8;
+      *reinterpret_cast<bf16x8*>(&sTm[1][i * LDH + j0]) = l8;
+    }
+    __syncthreads();  // A and Tm (f32) are dead: v^T goes in their place
+    for (int d = tid; d < D; d += kNT)
+      conv_channel<Act, K>(p, si, t0, nc, 2 * p.Hk * D + h * D + d, sVt + d * LDL, 1);
+    __syncthreads();
+    // Tm rows 16 tb + li for both products: as the A operand of U and as the
+    // B operand of W^T (the two lane layouts coincide).
+    bf16x8 th[NTL][2], tl[NTL][2];
+#pragma unroll
+    for (int tb = 0; tb < NTL; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        th[tb][ks] = ld8(&sTm[0][(16 * tb + li) * LDH + 32 * ks + 8 * lk]);
+        tl[tb][ks] = ld8(&sTm[1][(16 * tb + li) * LDH + 32 * ks + 8 * lk]);
+      }
+    for (int db = wave; db < NDB; db += kNW) {
+      const int d = 16 * db + li;
+      bf16x8 kh[2], kl[2], vh[2], vl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float kv[8], vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = 32 * ks + 8 * lk + e;
+          kv[e] = sSc[k] * sK[k * LDD + d];
+          vv[e] = sBeta[k] * sVt[d * LDL + k];
+        }
+        split8(kv, kh[ks], kl[ks]);
+        split8(vv, vh[ks], vl[ks]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < NTL; ++tb) {
+        // W^T tile: rows d (block db), columns token (block tb)
+        Acc3 aw = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
+        // U tile: rows token (block tb), columns d (block db)
+        Acc3 au = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          mfma3(aw, kh[ks], kl[ks], th[tb][ks], tl[tb][ks]);
+          mfma3(au, th[tb][ks], tl[tb][ks], vh[ks], vl[ks]);
+        }
+        const f32x4 wt = -fold(aw);   // -W[token 16 tb + li][d 16 db + 4 lk + e]
+        const size_t wo = frag_at(gh, kL, D, 16 * tb + li, 16 * db + 4 * lk);
+        store_split4(p.s.w[0] + wo, p.s.w[1] + wo, wt);
+        // U tile in the accumulator layout of the state kernel: block
+        // (d block db, token block tb), lane li + 16 lk
+        *reinterpret_cast<f32x4*>(p.s.ut + (((gh * NDB + db) * NTL + tb) * 64 + lane) * 4) = fold(au);
+      }
     }
     __syncthreads();
   }
@@ -516,294 +625,241 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
 constexpr int kSW = 8;             // waves of the state kernel
 constexpr int kSNT = 64 * kSW;
 
-// x * sigmoid(x) with the hardware exp and reciprocal (a few ulp).
-__device__ __forceinline__ float silu_fast(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
-
-// Wave roles in the state kernel (8 waves; token-row block orb = wave % 4):
-//   waves 0-3  X = K S, R = beta (V - e^gamma X), V' = Tm R   (load k_hat, Tm)
-//   waves 4-7  Y = Q S, O = e^gamma Y + P V'                  (load q_hat, P)
-//   wave w < D/16 also owns state row block w (both column blocks) and
-//   loads that block's k_hat^T rows.
-// so every operand fragment of a chunk is fetched once per workgroup.
-// Operands of one chunk held in registers by one wave; the next chunk's
-// are fetched into the same registers right after their last use.
-template <typename Act, int NKS, int K>
+// Operands of one chunk held in registers by one wave of the state kernel;
+// the next chunk's are fetched into the same registers right after their
+// last use.  The same registers serve both wave roles:
+//   waves 0-3 (the recurrence)  fa = -W rows, fb = k_hat^T rows of the owned
+//                               state row blocks, u = U tiles
+//   waves 4-7 (the outputs)     fa = q_hat rows, fb[0] = P rows
+template <int NKS, int RBW, int NCB>
 struct ChunkOps {
-  bf16x8 fr[NKS][2];   // k_hat (waves 0-3) or q_hat (waves 4-7): hi, lo
-  bf16x8 tp[2][2];     // Tm (waves 0-3) or P (waves 4-7): [k-step][hi, lo]
-  bf16x8 kt[2][2];     // k_hat^T rows of the owned state row block
-  typename act_io<Act>::raw_t vraw[2][K + 3];   // conv inputs, unconverted
-  uint32_t vuse;                                // bit cb*(K+3)+k: vraw[cb][k] is input
-  float gam, beta;     // row `lane` of the chunk
-  float glast;
+  bf16x8 fa[NKS][2];
+  bf16x8 fb[RBW][2][2];   // [row block][k-step][hi, lo]
+  f32x4 u[NCB];           // token rows i0 .. i0+3 of column 16 cb + li
+  f32x4 gam;              // gamma at rows i0 .. i0+3
+  float glast;            // gamma at the chunk's last token
 };
 
-template <typename Act, int D, int DVT, int K>
+// One workgroup per (sequence, V-head, 16 NCB state columns), one pass over
+// the sequence's chunks (chunk recurrence of the WY form: V' = U - W S,
+// S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) V', O = e^gamma Q S + P V').
+// Waves 0-3 carry the recurrence; waves 4-7 compute the chunk's outputs from
+// the same S and V' tiles in LDS, beside it, so the serial chain per chunk
+// is two contractions and two barriers.  Every operand fetch is one
+// contiguous 1 KB fragment block per wave.
+template <typename Act, int D, int K, int NCB>
 __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   using io = act_io<Act>;
-  constexpr int NCB = DVT / 16;        // 16-wide column blocks of the tile
-  constexpr int NKS = D / 32;          // k-steps over dk
+  constexpr int DVT = 16 * NCB;        // state columns of the workgroup
+  constexpr int NKS = D / 32;          // k-steps over d
   constexpr int NRB = D / 16;          // 16-row blocks of the state tile
+  constexpr int RBW = (NRB + 3) / 4;   // state row blocks per recurrence wave
   constexpr int LS = D + 8;            // row length of the transposed state [j][d]
   constexpr int LR = kL + 8;           // row length of [j][token] tiles
-  static_assert(NCB == 2 && NRB <= kSW, "tiling");
-  __shared__ __attribute__((aligned(16))) __bf16 sS[2][DVT * LS];   // state, B operand
-  __shared__ __attribute__((aligned(16))) __bf16 sR[2][DVT * LR];   // R
+  __shared__ __attribute__((aligned(16))) __bf16 sS[2][DVT * LS];   // S_c, B operand
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][DVT * LR];   // V'
   __shared__ __attribute__((aligned(16))) __bf16 sD[2][DVT * LR];   // e^{gamma_L - gamma} V'
-  __shared__ float sEg[kL], sBeta[kL], sDec[kL];
 
   const int n = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * DVT;
   const SeqInfo si = seq_info(p, n);
   if (si.slot < 0) return;
   const int m = h / p.r;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
-  const bool roleA = wave < 4;
-  const int orb = wave & 3;                    // token-row block
-  const bool ownsS = wave < NRB;               // state row block `wave`
-  const int i0 = 16 * orb + 4 * lk;            // first of this lane's four token rows
-  const int vch0 = 2 * p.Hk * D + h * D + col0 + li;   // v channel of column block 0
+  const bool rec = wave < 4;                   // recurrence wave
+  const int w4 = wave & 3;                     // token-row block (and state row block)
+  const int i0 = 16 * w4 + 4 * lk;             // first of this lane's four token rows
   float* Sg = p.rec + ((size_t)si.slot * p.Hv + h) * D * D;
   const size_t cbase = si.len > 0 ? (size_t)p.s.chunk_base[n] : 0;
   const int nchunks = (si.len + kL - 1) / kL;
 
-  float wt[NCB][K];
+  f32x4 S[RBW][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
+  for (int q = 0; q < RBW; ++q) {
+    const int rb = w4 + 4 * q;
 #pragma unroll
-    for (int k = 0; k < K; ++k) wt[cb][k] = io::load(p.conv_w, (size_t)(vch0 + 16 * cb) * K + k);
-
-  f32x4 S[NCB];
+    for (int cb = 0; cb < NCB; ++cb) {
+      S[q][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (rec && rb < NRB)
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ownsS)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = Sg[(size_t)(16 * wave + 4 * lk + e) * D + col0 + 16 * cb + li];
-        S[cb][e] = si.init ? v : 0.f;
-      }
+        for (int e = 0; e < 4; ++e) {
+          const float v = Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li];
+          S[q][cb][e] = si.init ? v : 0.f;
+        }
+    }
   }
 
   // Loads are unconditional within a wave's role (chunk index clamped), so
   // the prefetch of chunk c+1 never introduces a branch and its wait.
-  auto load_fr = [&](ChunkOps<Act, NKS, K>& o, int c) {
-    const size_t gk = (cbase + c) * p.Hk + m;
-    const size_t ro = (gk * kL + 16 * orb + li) * D + 8 * lk;
-    const __bf16* hi = roleA ? p.s.kh[0] : p.s.qh[0];
-    const __bf16* lo = roleA ? p.s.kh[1] : p.s.qh[1];
+  auto load_fa = [&](ChunkOps<NKS, RBW, NCB>& o, int c) {
+    const size_t mat = rec ? (cbase + c) * p.Hv + h : (cbase + c) * p.Hk + m;
+    const __bf16* hi = rec ? p.s.w[0] : p.s.qh[0];
+    const __bf16* lo = rec ? p.s.w[1] : p.s.qh[1];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      o.fr[ks][0] = ld8(hi + ro + 32 * ks);
-      o.fr[ks][1] = ld8(lo + ro + 32 * ks);
+      const size_t at = frag_lane(mat * (4 * NKS) + w4 * NKS + ks, lane);
+      o.fa[ks][0] = ld8(hi + at);
+      o.fa[ks][1] = ld8(lo + at);
     }
   };
-  auto load_tp = [&](ChunkOps<Act, NKS, K>& o, int c) {
-    const size_t gh = (cbase + c) * p.Hv + h;
-    const size_t ro = (gh * kL + 16 * orb + li) * kL + 8 * lk;
-    const __bf16* hi = roleA ? p.s.tm[0] : p.s.pm[0];
-    const __bf16* lo = roleA ? p.s.tm[1] : p.s.pm[1];
+  auto load_fb = [&](ChunkOps<NKS, RBW, NCB>& o, int c) {
+    const __bf16* hi = rec ? p.s.kt[0] : p.s.pm[0];
+    const __bf16* lo = rec ? p.s.kt[1] : p.s.pm[1];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      o.tp[ks][0] = ld8(hi + ro + 32 * ks);
-      o.tp[ks][1] = ld8(lo + ro + 32 * ks);
-    }
-  };
-  auto load_kt = [&](ChunkOps<Act, NKS, K>& o, int c) {
-    const size_t gk = (cbase + c) * p.Hk + m;
-    const size_t ro = (gk * D + 16 * (ownsS ? wave : 0) + li) * kL + 8 * lk;
+    for (int q = 0; q < RBW; ++q) {
+      if (!rec && q > 0) break;   // uniform: output waves need one P row block
+      const int rb = min(w4 + 4 * q, NRB - 1);
+      const size_t blk0 = rec ? (((cbase + c) * p.Hk + m) * NRB + rb) * 2
+                              : (((cbase + c) * p.Hv + h) * 4 + w4) * 2;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      o.kt[ks][0] = ld8(p.s.kt[0] + ro + 32 * ks);
-      o.kt[ks][1] = ld8(p.s.kt[1] + ro + 32 * ks);
+      for (int ks = 0; ks < 2; ++ks) {
+        const size_t at = frag_lane(blk0 + ks, lane);
+        o.fb[q][ks][0] = ld8(hi + at);
+        o.fb[q][ks][1] = ld8(lo + at);
+      }
     }
   };
-  const ChanReader<Act, K> vrd[NCB] = {ChanReader<Act, K>(p, si, vch0),
-                                       ChanReader<Act, K>(p, si, vch0 + 16)};
-  auto load_misc = [&](ChunkOps<Act, NKS, K>& o, int c) {
-    const int t0 = c * kL, nc = min(kL, si.len - t0);
+  auto load_misc = [&](ChunkOps<NKS, RBW, NCB>& o, int c) {
+    const int nc = min(kL, si.len - c * kL);
     const size_t gh = (cbase + c) * p.Hv + h;
-    o.glast = p.s.gam[gh * kL + nc - 1];
-    o.gam = p.s.gam[gh * kL + lane];
-    o.beta = p.s.beta[gh * kL + lane];
-    if (roleA) {
-      uint32_t bits = 0;
+    if (rec)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int k = 0; k < K + 3; ++k) {
-          const int pos = t0 + i0 - (K - 1) + k;  // relative to the sequence start
-          bool use;
-          o.vraw[cb][k] = vrd[cb].fetch(pos, pos < t0 + nc, use);
-          bits |= (uint32_t)use << (cb * (K + 3) + k);
-        }
-      o.vuse = bits;
-    }
+        o.u[cb] = *reinterpret_cast<const f32x4*>(
+            p.s.ut + (((gh * NRB + col0 / 16 + cb) * 4 + w4) * 64 + lane) * 4);
+    o.gam = *reinterpret_cast<const f32x4*>(p.s.gam + gh * kL + i0);
+    o.glast = p.s.gam[gh * kL + nc - 1];
   };
 
-  ChunkOps<Act, NKS, K> ops;
-  if (nchunks > 0) {
-    load_fr(ops, 0);
-    load_tp(ops, 0);
-    if (ownsS) load_kt(ops, 0);
+  // S_0 into LDS as hi/lo bf16, columns major
+  if (rec)
+#pragma unroll
+    for (int q = 0; q < RBW; ++q) {
+      const int rb = w4 + 4 * q;
+      if (rb < NRB)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            __bf16 hi, lo;
+            split_bf16(S[q][cb][e], hi, lo);
+            sS[0][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = hi;
+            sS[1][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = lo;
+          }
+    }
+  ChunkOps<NKS, RBW, NCB> ops;
+  if (nchunks > 0) {  // same issue order as in the loop (see its waits)
     load_misc(ops, 0);
+    load_fa(ops, 0);
+    load_fb(ops, 0);
   }
+  __syncthreads();
+
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kL, nc = min(kL, si.len - t0);
     const long long tok0 = si.begin + t0;
     const int cn = min(c + 1, nchunks - 1);  // chunk whose operands are prefetched
-    __syncthreads();  // the previous chunk is done with every LDS tile
-    if (tid < kL) {
-      const bool ok = tid < nc;
-      sEg[tid] = ok ? __expf(ops.gam) : 0.f;
-      sBeta[tid] = ok ? ops.beta : 0.f;
-      sDec[tid] = ok ? __expf(ops.glast - ops.gam) : 0.f;
-    }
-    const float egl = __expf(ops.glast);
-    float v4[NCB][4];
-    if (roleA)
+    // U and gamma are needed first: take them and refetch for the next chunk
+    // at once, so their loads are the oldest outstanding ones a chunk later
+    f32x4 u[NCB];
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        float xr[K + 3];
-#pragma unroll
-        for (int k = 0; k < K + 3; ++k)
-          xr[k] = (ops.vuse >> (cb * (K + 3) + k)) & 1u ? io::from_raw(ops.vraw[cb][k]) : 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float acc = 0.f;
-#pragma unroll
-          for (int k = 0; k < K; ++k) acc = fmaf(wt[cb][k], xr[e + k], acc);
-          v4[cb][e] = i0 + e < nc ? silu_fast(acc) : 0.f;
-        }
-      }
-    if (ownsS)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          __bf16 hi, lo;
-          split_bf16(S[cb][e], hi, lo);
-          const int idx = (16 * cb + li) * LS + 16 * wave + 4 * lk + e;
-          sS[0][idx] = hi;
-          sS[1][idx] = lo;
-        }
-    __syncthreads();
+    for (int cb = 0; cb < NCB; ++cb) u[cb] = ops.u[cb];
+    const f32x4 gam = ops.gam;
+    const float glast = ops.glast;
     load_misc(ops, cn);
-
-    // X = K S (waves 0-3) or Y = Q S (waves 4-7) for token-row block orb
-    f32x4 XY[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) XY[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
-        XY[cb] = mfma3(ops.fr[ks][0], ops.fr[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]), XY[cb]);
-      }
-    load_fr(ops, cn);
+    // phase 1: V' = U - W S_c (recurrence waves) / Y = Q S_c (output waves)
     f32x4 O[NCB];
-    if (roleA) {
-      // R = beta (V - e^gamma X) -> LDS
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int j = 16 * cb + li;
+    for (int cb = 0; cb < NCB; ++cb) {
+      Acc3 acc = acc3(rec ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          const float r = sBeta[i] * (v4[cb][e] - sEg[i] * XY[cb][e]);
-          __bf16 hi, lo;
-          split_bf16(r, hi, lo);
-          sR[0][j * LR + i] = hi;
-          sR[1][j * LR + i] = lo;
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
+        mfma3(acc, ops.fa[ks][0], ops.fa[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]));
       }
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[cb][e] = sEg[i0 + e] * XY[cb][e];
-    }
-    __syncthreads();
-    if (roleA) {
-      // V' = Tm R -> LDS, plain and scaled by e^{gamma_last - gamma}
-      f32x4 Vp[NCB];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) Vp[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-          Vp[cb] = mfma3(ops.tp[ks][0], ops.tp[ks][1], ld8(&sR[0][bo]), ld8(&sR[1][bo]), Vp[cb]);
-        }
-      load_tp(ops, cn);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int j = 16 * cb + li;
+      const f32x4 r1 = fold(acc);
+      if (rec) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
+          const int j = 16 * cb + li, i = i0 + e;
           __bf16 hi, lo;
-          split_bf16(Vp[cb][e], hi, lo);
+          split_bf16(r1[e], hi, lo);
           sV[0][j * LR + i] = hi;
           sV[1][j * LR + i] = lo;
-          split_bf16(sDec[i] * Vp[cb][e], hi, lo);
+          split_bf16(__expf(glast - gam[e]) * r1[e], hi, lo);
           sD[0][j * LR + i] = hi;
           sD[1][j * LR + i] = lo;
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[cb][e] = __expf(gam[e]) * r1[e];
       }
     }
-    __syncthreads();
-    if (!roleA) {
-      // O += P V'  and store the pre-norm output
+    load_fa(ops, cn);
+    __syncthreads();  // V' is in LDS; every read of S_c is done
+    if (rec) {
+      // phase 2: S <- e^{gamma_L} S + K^T (e^{gamma_L - gamma} V')
+      const float egl = __expf(glast);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int q = 0; q < RBW; ++q) {
+        const int rb = w4 + 4 * q;
+        if (rb < NRB)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-          O[cb] = mfma3(ops.tp[ks][0], ops.tp[ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]), O[cb]);
-        }
-      load_tp(ops, cn);
+          for (int cb = 0; cb < NCB; ++cb) {
+            Acc3 as = acc3(S[q][cb] * egl);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+            for (int ks = 0; ks < 2; ++ks) {
+              const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+              mfma3(as, ops.fb[q][ks][0], ops.fb[q][ks][1], ld8(&sD[0][bo]), ld8(&sD[1][bo]));
+            }
+            S[q][cb] = fold(as);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          if (i < nc)
-            p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li] = O[cb][e];
-        }
-    }
-    if (ownsS) {
-      // S <- e^{gamma_last} S + K^T (e^{gamma_last - gamma} V')
+            for (int e = 0; e < 4; ++e) {
+              __bf16 hi, lo;
+              split_bf16(S[q][cb][e], hi, lo);
+              sS[0][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = hi;
+              sS[1][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = lo;
+            }
+          }
+      }
+    } else {
+      // O += P V', stored as the pre-norm output
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        S[cb] *= egl;
+        Acc3 ao = acc3(O[cb]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-          S[cb] = mfma3(ops.kt[ks][0], ops.kt[ks][1], ld8(&sD[0][bo]), ld8(&sD[1][bo]), S[cb]);
+          mfma3(ao, ops.fb[0][ks][0], ops.fb[0][ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]));
+        }
+        const f32x4 o = fold(ao);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          if (i < nc) p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li] = o[e];
         }
       }
-      load_kt(ops, cn);
     }
+    load_fb(ops, cn);
+    __syncthreads();  // S_{c+1} is in LDS; every read of V' is done
   }
 
-  if (ownsS)
+  if (rec)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int q = 0; q < RBW; ++q) {
+      const int rb = w4 + 4 * q;
+      if (rb < NRB)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Sg[(size_t)(16 * wave + 4 * lk + e) * D + col0 + 16 * cb + li] = S[cb][e];
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li] = S[q][cb][e];
+    }
 
   // Final conv window = the last K raw inputs of [window ; tokens], for this
   // tile's v channels, plus the q/k channels of K-head m from tile 0 of its
   // first V-head.  No other workgroup reads these channels of the window
-  // (the prep kernel, an earlier launch, read the q/k ones).
-  __syncthreads();
+  // (the prep kernel, an earlier launch, read all of them).
   {
     const bool qk = blockIdx.z == 0 && h % p.r == 0;
     const int nch = DVT + (qk ? 2 * D : 0);
@@ -875,12 +931,34 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------------ launch
 
-template <typename Act, int D, int DVT, int K>
+// 16-column blocks per state workgroup: the widest tile (at most 64 columns,
+// which fits the registers) that still gives about one workgroup per CU.
+// Every tile re-reads the chunk operands of its head, so wider tiles cut that
+// traffic; narrower ones spread a few long sequences over more CUs.
+static int state_col_blocks(int N, int Hv, int D) {
+  int tiles = D > 64 ? D / 64 : 1;
+  while (tiles < D / 16 && (long long)N * Hv * tiles < 256) tiles *= 2;
+  return D / 16 / tiles;
+}
+
+template <typename Act, int D, int K, int NCB>
+static void launch_state(const PrefillParams& p, hipStream_t st) {
+  // tiles of one (sequence, head) are N * Hv workgroups apart: with N * Hv a
+  // multiple of 8 they share an XCD and its L2 for the chunk operands
+  prefill_state_kernel<Act, D, K, NCB><<<dim3(p.N, p.Hv, D / (16 * NCB)), kSNT, 0, st>>>(p);
+}
+
+template <typename Act, int D, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
   prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
   if (max_chunks > 0)
     prefill_prep_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
-  prefill_state_kernel<Act, D, DVT, K><<<dim3(p.N, p.Hv, D / DVT), kSNT, 0, st>>>(p);
+  switch (state_col_blocks(p.N, p.Hv, D)) {
+    case 1: launch_state<Act, D, K, 1>(p, st); break;
+    case 2: launch_state<Act, D, K, 2>(p, st); break;
+    case 4: if constexpr (D >= 64) launch_state<Act, D, K, 4>(p, st); break;
+    default: return hipErrorInvalidValue;
+  }
   if (max_chunks > 0)
     prefill_norm_kernel<Act, D><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
   return hipGetLastError();
@@ -888,11 +966,10 @@ static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_
 
 template <typename Act, int D>
 static hipError_t prefill_k(const PrefillParams& p, int K, int mc, hipStream_t st) {
-  constexpr int DVT = 32;
   switch (K) {
-    case 2: return prefill_run<Act, D, DVT, 2>(p, mc, st);
-    case 3: return prefill_run<Act, D, DVT, 3>(p, mc, st);
-    case 4: return prefill_run<Act, D, DVT, 4>(p, mc, st);
+    case 2: return prefill_run<Act, D, 2>(p, mc, st);
+    case 3: return prefill_run<Act, D, 3>(p, mc, st);
+    case 4: return prefill_run<Act, D, 4>(p, mc, st);
     default: return hipErrorInvalidValue;
   }
 }
