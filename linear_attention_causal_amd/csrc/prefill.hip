@@ -193,35 +193,77 @@ struct ChanReader {
     const float v = act_io<Act>::from_raw(fetch(pos, valid, use));
     return use ? v : 0.f;
   }
+
+  // The 16 bytes starting at this channel (16 / element-size consecutive
+  // channels) at `pos`, same rules; the caller zeroes them when !use.
+  __device__ __forceinline__ u32x4 fetch16(int pos, bool valid, bool& use) const {
+    const bool in_x = pos >= 0;
+    use = valid & (in_x ? pos < len : (init & (pos >= -K)));
+    const int pc = use ? pos : (in_x ? 0 : -1);
+    const char* a = (in_x ? xb : wb) + (long long)pc * stride;
+    return *reinterpret_cast<const u32x4*>(a);
+  }
 };
 
-// Causal conv + SiLU of one channel over tokens t0 .. t0+nc-1 of a sequence;
-// out[i * ld] for i < kL (rows >= nc get zero).  All kL + K - 1 inputs are
-// requested before any arithmetic so that their latencies overlap.
-template <typename Act, int K>
-__device__ __forceinline__ void conv_channel(const PrefillParams& p, const SeqInfo& si,
-                                             int t0, int nc, int ch, float* out, int ld) {
-  using io = act_io<Act>;
-  float wt[K];
+// 16 raw bytes as 16 / element-size floats.
+template <typename Act>
+__device__ __forceinline__ void unpack16(u32x4 r, float* f) {
+  if constexpr (sizeof(Act) == 2) {
 #pragma unroll
-  for (int j = 0; j < K; ++j) wt[j] = io::load(p.conv_w, (size_t)ch * K + j);
-  float xs[kL + K - 1];  // positions t0-(K-1) .. t0+kL-1
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(r[i] << 16);
+      f[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(r[i]);
+  }
+}
+
+// Causal conv + SiLU of one 16-byte run of channels (V = 16 / element-size
+// consecutive channels from ch, a multiple of V) over tokens i_off ..
+// i_off+TPT-1 of the chunk starting at sequence position t0; tokens at or
+// past nc give zero.  All TPT + K - 1 input runs and the weights are
+// requested before any arithmetic, so one thread issues a handful of 16-byte
+// loads instead of one load per element.
+template <typename Act, int K, int TPT>
+__device__ __forceinline__ void conv_tile(const PrefillParams& p, const SeqInfo& si, int t0,
+                                          int nc, int i_off, int ch,
+                                          float (&out)[TPT][16 / sizeof(Act)]) {
+  constexpr int V = 16 / sizeof(Act);
   const ChanReader<Act, K> rd(p, si, ch);
+  u32x4 raw[TPT + K - 1];
+  bool use[TPT + K - 1];
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) xs[j] = rd(t0 - (K - 1) + j);
-  const size_t base = (size_t)(si.begin + t0) * p.C + ch;
+  for (int j = 0; j < TPT + K - 1; ++j) {
+    const int r = i_off - (K - 1) + j;   // relative to the chunk start
+    raw[j] = rd.fetch16(t0 + r, r < nc, use[j]);
+  }
+  // weights of the V channels: V * K consecutive elements = K runs of 16 bytes
+  u32x4 wraw[K];
+  const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.conv_w) +
+                                                   (size_t)ch * K * sizeof(Act));
 #pragma unroll
-  for (int i = 0; i < kL; ++i) {  // clamped address, then select: no branch per load
-    const float v = io::load(p.x, base + (size_t)min(i, nc - 1) * p.C);
-    xs[K - 1 + i] = i < nc ? v : 0.f;
+  for (int k = 0; k < K; ++k) wraw[k] = wp[k];
+  float wt[V * K];   // wt[v * K + k]
+#pragma unroll
+  for (int k = 0; k < K; ++k) unpack16<Act>(wraw[k], wt + k * V);
+  float xs[TPT + K - 1][V];
+#pragma unroll
+  for (int j = 0; j < TPT + K - 1; ++j) {
+    unpack16<Act>(raw[j], xs[j]);
+#pragma unroll
+    for (int v = 0; v < V; ++v) xs[j][v] = use[j] ? xs[j][v] : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < kL; ++i) {
-    float acc = 0.f;
+  for (int t = 0; t < TPT; ++t)
 #pragma unroll
-    for (int j = 0; j < K; ++j) acc = fmaf(wt[j], xs[i + j], acc);
-    out[i * ld] = i < nc ? silu(acc) : 0.f;
-  }
+    for (int v = 0; v < V; ++v) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc = fmaf(wt[v * K + k], xs[t + k][v], acc);
+      out[t][v] = i_off + t < nc ? silu_fast(acc) : 0.f;
+    }
 }
 
 // --------------------------------------------------------------- MFMA helpers
@@ -435,7 +477,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   __shared__ float sG[kL * LDL];                                // K K^T
   __shared__ float sQK[kL * LDL];                               // Q K^T
   __shared__ __attribute__((aligned(16))) __bf16 sTm[2][kL * LDH];   // Tm hi, lo
-  __shared__ float sGam[kL], sBeta[kL], sSc[kL];
+  __shared__ float sGam[kL], sBeta[kL], sSc[kL], sRq[kL], sRk[kL];
   float* sQ = sR1;
 
   const int c = blockIdx.x, n = blockIdx.y, m = blockIdx.z;
@@ -448,28 +490,55 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
-  // conv + SiLU of q_m and k_m
-  for (int e = tid; e < 2 * D; e += kNT) {
-    if (e < D)
-      conv_channel<Act, K>(p, si, t0, nc, m * D + e, sQ + e, LDD);
-    else
-      conv_channel<Act, K>(p, si, t0, nc, (p.Hk + m) * D + (e - D), sK + (e - D), LDD);
+  // gate inputs of this chunk for the K-head's V-heads, requested up front
+  float a_in[4], b_in[4];
+  if (wave == 0) {
+    const long long tk = tok0 + min(lane, nc - 1);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const int h = m * p.r + min(hh, p.r - 1);
+      a_in[hh] = io::load(p.a, (size_t)tk * p.Hv + h);
+      b_in[hh] = io::load(p.b, (size_t)tk * p.Hv + h);
+    }
+  }
+  // conv + SiLU of q_m and k_m: thread = (16-byte channel run, run of tokens)
+  {
+    constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kNT;
+    static_assert(kNT % G == 0 && TPT >= 1, "q/k conv split");
+    const int grp = tid % G, i_off = (tid / G) * TPT;
+    const int c0 = grp * V;                      // 0 .. 2D-1: q then k
+    const int ch = c0 < D ? m * D + c0 : (p.Hk + m) * D + (c0 - D);
+    float* dst = c0 < D ? sQ + c0 : sK + (c0 - D);
+    float out[TPT][V];
+    conv_tile<Act, K, TPT>(p, si, t0, nc, i_off, ch, out);
+#pragma unroll
+    for (int t = 0; t < TPT; ++t)
+#pragma unroll
+      for (int v = 0; v < V; v += 4)
+        *reinterpret_cast<f32x4*>(dst + (i_off + t) * LDD + v) =
+            f32x4{out[t][v], out[t][v + 1], out[t][v + 2], out[t][v + 3]};
   }
   __syncthreads();
-  // l2norm (q also scaled)
-  for (int i = wave; i < nc; i += kNW) {
+  // l2 norms as per-row factors (q's includes the 1/sqrt(dk) scale), applied
+  // where the rows are used: four lanes per row
+  {
+    constexpr int QD = D / 4;
+    const int i = tid >> 2, part = tid & 3;
     float sq = 0.f, sk = 0.f;
-    for (int d = lane; d < D; d += 64) {
+#pragma unroll 8
+    for (int d = part * QD; d < (part + 1) * QD; ++d) {
       const float qv = sQ[i * LDD + d], kv = sK[i * LDD + d];
       sq = fmaf(qv, qv, sq);
       sk = fmaf(kv, kv, sk);
     }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float rq = p.scale / sqrtf(sq + p.l2eps), rk = 1.0f / sqrtf(sk + p.l2eps);
-    for (int d = lane; d < D; d += 64) {
-      sQ[i * LDD + d] *= rq;
-      sK[i * LDD + d] *= rk;
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1) {
+      sq += __shfl_xor(sq, off, 64);
+      sk += __shfl_xor(sk, off, 64);
+    }
+    if (part == 0) {
+      sRq[i] = p.scale / sqrtf(sq + p.l2eps);
+      sRk[i] = 1.0f / sqrtf(sk + p.l2eps);
     }
   }
   __syncthreads();
@@ -478,8 +547,11 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     const size_t gk = g * p.Hk + m;
     for (int u = tid; u < kL * (D / 8); u += kNT) {
       const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sQ[i * LDD + d0 + e] * sRq[i];
       bf16x8 h, l;
-      split8(sQ + i * LDD + d0, h, l);
+      split8(v, h, l);
       const size_t at = frag_at(gk, kL, D, i, d0);
       *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
       *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;
@@ -488,7 +560,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d];
+      for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d] * sRk[i0 + e];
       bf16x8 h, l;
       split8(v, h, l);
       const size_t at = frag_at(gk, D, kL, d, i0);
@@ -511,10 +583,15 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       split8(sK + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
       mfma3(acc, ah, al, bh, bl);
     }
-    const f32x4 r = fold(acc);
+    const f32x4 r = fold(acc);   // unnormalized rows: scale by the row factors
     float* dst = isG ? sG : sQK;
+    const float* ra = isG ? sRk : sRq;
+    const float rj = sRk[16 * J + li];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[(16 * I + 4 * lk + e) * LDL + 16 * J + li] = r[e];
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * I + 4 * lk + e;
+      dst[i * LDL + 16 * J + li] = r[e] * ra[i] * rj;
+    }
   }
   __syncthreads();  // the q tile is free from here on (reused as A, Tm, then v^T)
 
@@ -525,10 +602,10 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     const int h = m * p.r + hh;
     const size_t gh = g * p.Hv + h;
     if (wave == 0) {
+      const float av = hh == 0 ? a_in[0] : hh == 1 ? a_in[1] : hh == 2 ? a_in[2] : a_in[3];
+      const float bb = hh == 0 ? b_in[0] : hh == 1 ? b_in[1] : hh == 2 ? b_in[2] : b_in[3];
       float gv = 0.f, bv = 0.f;
-      if (lane < nc)
-        gates(p.A_log[h], p.dt_bias[h], io::load(p.a, (size_t)(tok0 + lane) * p.Hv + h),
-              io::load(p.b, (size_t)(tok0 + lane) * p.Hv + h), gv, bv);
+      if (lane < nc) gates(p.A_log[h], p.dt_bias[h], av, bb, gv, bv);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(gv, off, 64);
@@ -536,14 +613,14 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       }
       sGam[lane] = gv;
       sBeta[lane] = bv;
-      sSc[lane] = bv * expf(gv);
+      sSc[lane] = bv * expf(gv) * sRk[lane];   // W row factor, k's l2 norm folded in
       p.s.gam[gh * kL + lane] = gv;
     }
     __syncthreads();
     // A (for the inverse) and P (written out as fragments)
     for (int idx = tid; idx < kL * kL; idx += kNT) {
       const int i = idx / kL, j = idx - i * kL;
-      sA[i * LDL + j] = j < i ? sBeta[i] * expf(sGam[i] - sGam[j]) * sG[i * LDL + j] : 0.f;
+      sA[i * LDL + j] = j < i ? sBeta[i] * __expf(sGam[i] - sGam[j]) * sG[i * LDL + j] : 0.f;
     }
     for (int u = tid; u < kL * (kL / 8); u += kNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
@@ -551,7 +628,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        v[e] = j <= i ? expf(sGam[i] - sGam[j]) * sQK[i * LDL + j] : 0.f;
+        v[e] = j <= i ? __expf(sGam[i] - sGam[j]) * sQK[i * LDL + j] : 0.f;
       }
       bf16x8 h8, l8;
       split8(v, h8, l8);
@@ -569,8 +646,17 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       *reinterpret_cast<bf16x8*>(&sTm[1][i * LDH + j0]) = l8;
     }
     __syncthreads();  // A and Tm (f32) are dead: v^T goes in their place
-    for (int d = tid; d < D; d += kNT)
-      conv_channel<Act, K>(p, si, t0, nc, 2 * p.Hk * D + h * D + d, sVt + d * LDL, 1);
+    {  // thread = (16-byte channel run, run of tokens), written transposed
+      constexpr int V = 16 / sizeof(Act), G = D / V, TPT = kL * G / kNT;
+      static_assert(kNT % G == 0 && TPT >= 1, "v conv split");
+      const int grp = tid % G, i_off = (tid / G) * TPT;
+      float out[TPT][V];
+      conv_tile<Act, K, TPT>(p, si, t0, nc, i_off, 2 * p.Hk * D + h * D + grp * V, out);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int t = 0; t < TPT; ++t) sVt[(grp * V + v) * LDL + i_off + t] = out[t][v];
+    }
     __syncthreads();
     // Tm rows 16 tb + li for both products: as the A operand of U and as the
     // B operand of W^T (the two lane layouts coincide).
