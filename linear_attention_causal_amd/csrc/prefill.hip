@@ -407,52 +407,43 @@ __device__ __forceinline__ f32x4 mm16(const float* A, int lda, const float* B, i
 
 // Tm = (I + A)^{-1} for strictly lower-triangular A [64][LDL] in LDS, blocked
 // by 16: the four diagonal blocks by forward substitution (one lane per
-// column), then T_ij = -T_ii sum_{j<=k<i} A_ik T_kj by distance i - j.
-// Called by all four waves; ends with the result in sT.
+// column), then wave jb walks down column block jb,
+//   T_ib,jb = -T_ib,ib sum_{jb <= kb < ib} A_ib,kb T_kb,jb,   ib = jb+1 .. 3,
+// reading only its own earlier blocks and the diagonal ones.  Called by all
+// four waves; ends with the lower blocks of the result in sT (the strictly
+// upper blocks of sT are left as they are: the caller treats them as zero).
 template <int LDL>
 __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int tid) {
   const int lane = tid & 63, wave = wave_id();
-  const int li = lane & 15, lk = lane >> 4;
-  // strictly upper blocks are zero
-  for (int idx = tid; idx < kL * kL; idx += kNT) {
-    const int i = idx / kL, j = idx - i * kL;
-    if ((j >> 4) > (i >> 4)) sT[i * LDL + j] = 0.f;
-  }
   if (lane < 16) {
+    // column sweeps: once t_j is final, remove its term from every later row,
+    // so the dependency chain is 15 steps long
     const int b0 = 16 * wave, c = lane;
     float t[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = i == c ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) t[i] = i == c ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) acc = fmaf(-sA[(b0 + i) * LDL + b0 + j], t[j], acc);
-      t[i] = acc;
-    }
+    for (int j = 0; j < 15; ++j)
+#pragma unroll
+      for (int i = j + 1; i < 16; ++i) t[i] = fmaf(-sA[(b0 + i) * LDL + b0 + j], t[j], t[i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sT[(b0 + i) * LDL + b0 + c] = t[i];
   }
   __syncthreads();
-  float* M = sM + wave * 16 * 17;
+  const int li = lane & 15, lk = lane >> 4;
+  const int jb = wave;
+  float* M = sM + wave * 16 * 17;   // this wave's 16 x 16 staging tile
+  for (int ib = jb + 1; ib < 4; ++ib) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = jb; kb < ib; ++kb)
+      acc = mm16(sA + 16 * ib * LDL + 16 * kb, LDL, sT + 16 * kb * LDL + 16 * jb, LDL, acc, lane);
 #pragma unroll
-  for (int dist = 1; dist < 4; ++dist) {
-    const int jb = wave, ib = wave + dist;
-    const bool act = ib < 4;
-    if (act) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int kb = jb; kb < ib; ++kb)
-        acc = mm16(sA + 16 * ib * LDL + 16 * kb, LDL, sT + 16 * kb * LDL + 16 * jb, LDL, acc, lane);
+    for (int e = 0; e < 4; ++e) M[(4 * lk + e) * 17 + li] = acc[e];
+    acc = mm16(sT + 16 * ib * LDL + 16 * ib, LDL, M, 17, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) M[(4 * lk + e) * 17 + li] = acc[e];
-    }
-    __syncthreads();
-    if (act) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm16(sT + 16 * ib * LDL + 16 * ib, LDL, M, 17, acc, lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * ib + 4 * lk + e) * LDL + 16 * jb + li] = -acc[e];
-    }
-    __syncthreads();
+    for (int e = 0; e < 4; ++e) sT[(16 * ib + 4 * lk + e) * LDL + 16 * jb + li] = -acc[e];
   }
+  __syncthreads();
 }
 
 // One workgroup per (chunk, sequence, K-head).  Everything here depends on
@@ -491,7 +482,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   const int li = lane & 15, lk = lane >> 4;
 
   // gate inputs of this chunk for the K-head's V-heads, requested up front
-  float a_in[4], b_in[4];
+  float a_in[4], b_in[4], alog[4], dtb[4];
   if (wave == 0) {
     const long long tk = tok0 + min(lane, nc - 1);
 #pragma unroll
@@ -499,6 +490,8 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       const int h = m * p.r + min(hh, p.r - 1);
       a_in[hh] = io::load(p.a, (size_t)tk * p.Hv + h);
       b_in[hh] = io::load(p.b, (size_t)tk * p.Hv + h);
+      alog[hh] = p.A_log[h];
+      dtb[hh] = p.dt_bias[h];
     }
   }
   // conv + SiLU of q_m and k_m: thread = (16-byte channel run, run of tokens)
@@ -604,8 +597,10 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     if (wave == 0) {
       const float av = hh == 0 ? a_in[0] : hh == 1 ? a_in[1] : hh == 2 ? a_in[2] : a_in[3];
       const float bb = hh == 0 ? b_in[0] : hh == 1 ? b_in[1] : hh == 2 ? b_in[2] : b_in[3];
+      const float al = hh == 0 ? alog[0] : hh == 1 ? alog[1] : hh == 2 ? alog[2] : alog[3];
+      const float db = hh == 0 ? dtb[0] : hh == 1 ? dtb[1] : hh == 2 ? dtb[2] : dtb[3];
       float gv = 0.f, bv = 0.f;
-      if (lane < nc) gates(p.A_log[h], p.dt_bias[h], av, bb, gv, bv);
+      if (lane < nc) gates(al, db, av, bb, gv, bv);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(gv, off, 64);
@@ -617,18 +612,18 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       p.s.gam[gh * kL + lane] = gv;
     }
     __syncthreads();
-    // A (for the inverse) and P (written out as fragments)
-    for (int idx = tid; idx < kL * kL; idx += kNT) {
-      const int i = idx / kL, j = idx - i * kL;
-      sA[i * LDL + j] = j < i ? sBeta[i] * __expf(sGam[i] - sGam[j]) * sG[i * LDL + j] : 0.f;
-    }
+    // A (for the inverse; only its lower triangle is read) and P (written
+    // out as fragments), sharing one decay e^{gamma_i - gamma_j} per element
     for (int u = tid; u < kL * (kL / 8); u += kNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+      const float gi = sGam[i], bi = sBeta[i];
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        v[e] = j <= i ? __expf(sGam[i] - sGam[j]) * sQK[i * LDL + j] : 0.f;
+        const float dec = j <= i ? __expf(gi - sGam[j]) : 0.f;
+        sA[i * LDL + j] = j < i ? bi * dec * sG[i * LDL + j] : 0.f;
+        v[e] = dec * sQK[i * LDL + j];
       }
       bf16x8 h8, l8;
       split8(v, h8, l8);
@@ -640,8 +635,12 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTm[0][0]), tid);
     for (int u = tid; u < kL * (kL / 8); u += kNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+      const bool upper = (j0 >> 4) > (i >> 4);   // strictly upper block: zero
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = upper ? 0.f : sT[i * LDL + j0 + e];
       bf16x8 h8, l8;
-      split8(sT + i * LDL + j0, h8, l8);
+      split8(v, h8, l8);
       *reinterpret_cast<bf16x8*>(&sTm[0][i * LDH + j0]) = h8;
       *reinterpret_cast<bf16x8*>(&sTm[1][i * LDH + j0]) = l8;
     }
