@@ -223,48 +223,56 @@ __device__ __forceinline__ void unpack16(u32x4 r, float* f) {
 // Causal conv + SiLU of one 16-byte run of channels (V = 16 / element-size
 // consecutive channels from ch, a multiple of V) over tokens i_off ..
 // i_off+TPT-1 of the chunk starting at sequence position t0; tokens at or
-// past nc give zero.  All TPT + K - 1 input runs and the weights are
-// requested before any arithmetic, so one thread issues a handful of 16-byte
-// loads instead of one load per element.
+// past nc give zero.  fetch() requests all TPT + K - 1 input runs and the
+// weights (a handful of 16-byte loads instead of one load per element);
+// finish() waits for them and computes, so other work can go in between.
 template <typename Act, int K, int TPT>
-__device__ __forceinline__ void conv_tile(const PrefillParams& p, const SeqInfo& si, int t0,
-                                          int nc, int i_off, int ch,
-                                          float (&out)[TPT][16 / sizeof(Act)]) {
-  constexpr int V = 16 / sizeof(Act);
-  const ChanReader<Act, K> rd(p, si, ch);
+struct ConvTile {
+  static constexpr int V = 16 / sizeof(Act);
   u32x4 raw[TPT + K - 1];
-  bool use[TPT + K - 1];
-#pragma unroll
-  for (int j = 0; j < TPT + K - 1; ++j) {
-    const int r = i_off - (K - 1) + j;   // relative to the chunk start
-    raw[j] = rd.fetch16(t0 + r, r < nc, use[j]);
-  }
-  // weights of the V channels: V * K consecutive elements = K runs of 16 bytes
   u32x4 wraw[K];
-  const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.conv_w) +
-                                                   (size_t)ch * K * sizeof(Act));
+  uint32_t use;   // bit j: input run j is part of the input
+
+  __device__ __forceinline__ void fetch(const PrefillParams& p, const SeqInfo& si, int t0,
+                                        int nc, int i_off, int ch) {
+    const ChanReader<Act, K> rd(p, si, ch);
+    use = 0;
 #pragma unroll
-  for (int k = 0; k < K; ++k) wraw[k] = wp[k];
-  float wt[V * K];   // wt[v * K + k]
-#pragma unroll
-  for (int k = 0; k < K; ++k) unpack16<Act>(wraw[k], wt + k * V);
-  float xs[TPT + K - 1][V];
-#pragma unroll
-  for (int j = 0; j < TPT + K - 1; ++j) {
-    unpack16<Act>(raw[j], xs[j]);
-#pragma unroll
-    for (int v = 0; v < V; ++v) xs[j][v] = use[j] ? xs[j][v] : 0.f;
-  }
-#pragma unroll
-  for (int t = 0; t < TPT; ++t)
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < K; ++k) acc = fmaf(wt[v * K + k], xs[t + k][v], acc);
-      out[t][v] = i_off + t < nc ? silu_fast(acc) : 0.f;
+    for (int j = 0; j < TPT + K - 1; ++j) {
+      const int r = i_off - (K - 1) + j;   // relative to the chunk start
+      bool u;
+      raw[j] = rd.fetch16(t0 + r, r < nc, u);
+      use |= (uint32_t)u << j;
     }
-}
+    // weights of the V channels: V * K consecutive elements = K runs of 16 bytes
+    const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.conv_w) +
+                                                     (size_t)ch * K * sizeof(Act));
+#pragma unroll
+    for (int k = 0; k < K; ++k) wraw[k] = wp[k];
+  }
+
+  __device__ __forceinline__ void finish(int nc, int i_off, float (&out)[TPT][V]) const {
+    float wt[V * K];   // wt[v * K + k]
+#pragma unroll
+    for (int k = 0; k < K; ++k) unpack16<Act>(wraw[k], wt + k * V);
+    float xs[TPT + K - 1][V];
+#pragma unroll
+    for (int j = 0; j < TPT + K - 1; ++j) {
+      unpack16<Act>(raw[j], xs[j]);
+#pragma unroll
+      for (int v = 0; v < V; ++v) xs[j][v] = (use >> j) & 1u ? xs[j][v] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < TPT; ++t)
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc = fmaf(wt[v * K + k], xs[t + k][v], acc);
+        out[t][v] = i_off + t < nc ? silu_fast(acc) : 0.f;
+      }
+  }
+};
 
 // --------------------------------------------------------------- MFMA helpers
 
@@ -460,15 +468,16 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NKS = D / 32, NDB = D / 16;
   constexpr int LDH = kL + 8;   // bf16 row length of the split Tm
-  constexpr int R1A = kL * LDD, R1B = 2 * kL * LDL, R1C = D * LDL;
-  constexpr int R1 = R1A > R1B ? (R1A > R1C ? R1A : R1C) : (R1B > R1C ? R1B : R1C);
+  constexpr int R1A = kL * LDD, R1B = 2 * kL * LDL;
+  constexpr int R1 = R1A > R1B ? R1A : R1B;
   static_assert(kNW * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the Tm tiles");
-  __shared__ __attribute__((aligned(16))) float sR1[R1];        // q_hat; then A | Tm; then v^T
+  __shared__ __attribute__((aligned(16))) float sR1[R1];        // q_hat; then A | Tm
   __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k_hat rows
   __shared__ float sG[kL * LDL];                                // K K^T
   __shared__ float sQK[kL * LDL];                               // Q K^T
   __shared__ __attribute__((aligned(16))) __bf16 sTm[2][kL * LDH];   // Tm hi, lo
-  __shared__ float sGam[kL], sBeta[kL], sSc[kL], sRq[kL], sRk[kL];
+  __shared__ __attribute__((aligned(16))) float sVt[D * LDL];   // v^T of the current V-head
+  __shared__ float sGam[4][kL], sBeta[4][kL], sSc[4][kL], sRq[kL], sRk[kL];
   float* sQ = sR1;
 
   const int c = blockIdx.x, n = blockIdx.y, m = blockIdx.z;
@@ -481,19 +490,33 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
-  // gate inputs of this chunk for the K-head's V-heads, requested up front
-  float a_in[4], b_in[4], alog[4], dtb[4];
-  if (wave == 0) {
-    const long long tk = tok0 + min(lane, nc - 1);
+  // Gates of the K-head's V-heads m r + hh, four at a time, wave w taking
+  // hh0 + w: running sum gamma, beta, and the W row factor beta e^gamma / |k|
+  // into slot hh & 3.  The first group's inputs are requested up front.
+  const long long gate_tok = tok0 + min(lane, nc - 1);
+  auto gate_in = [&](int hh0, float& a_in, float& b_in, float& alog, float& dtb) {
+    const int h = m * p.r + hh0 + wave;
+    a_in = io::load(p.a, (size_t)gate_tok * p.Hv + h);
+    b_in = io::load(p.b, (size_t)gate_tok * p.Hv + h);
+    alog = p.A_log[h];
+    dtb = p.dt_bias[h];
+  };
+  auto gate_run = [&](int hh0, float a_in, float b_in, float alog, float dtb) {
+    const int hh = hh0 + wave, h = m * p.r + hh;
+    float gv = 0.f, bv = 0.f;
+    if (lane < nc) gates(alog, dtb, a_in, b_in, gv, bv);
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const int h = m * p.r + min(hh, p.r - 1);
-      a_in[hh] = io::load(p.a, (size_t)tk * p.Hv + h);
-      b_in[hh] = io::load(p.b, (size_t)tk * p.Hv + h);
-      alog[hh] = p.A_log[h];
-      dtb[hh] = p.dt_bias[h];
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(gv, off, 64);
+      if (lane >= off) gv += y;
     }
-  }
+    sGam[hh & 3][lane] = gv;
+    sBeta[hh & 3][lane] = bv;
+    sSc[hh & 3][lane] = bv * expf(gv) * sRk[lane];
+    p.s.gam[(g * p.Hv + h) * kL + lane] = gv;
+  };
+  float ga = 0.f, gb = 0.f, gal = 0.f, gdt = 0.f;
+  if (wave < p.r) gate_in(0, ga, gb, gal, gdt);
   // conv + SiLU of q_m and k_m: thread = (16-byte channel run, run of tokens)
   {
     constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kNT;
@@ -503,7 +526,9 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     const int ch = c0 < D ? m * D + c0 : (p.Hk + m) * D + (c0 - D);
     float* dst = c0 < D ? sQ + c0 : sK + (c0 - D);
     float out[TPT][V];
-    conv_tile<Act, K, TPT>(p, si, t0, nc, i_off, ch, out);
+    ConvTile<Act, K, TPT> ct;
+    ct.fetch(p, si, t0, nc, i_off, ch);
+    ct.finish(nc, i_off, out);
 #pragma unroll
     for (int t = 0; t < TPT; ++t)
 #pragma unroll
@@ -535,6 +560,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     }
   }
   __syncthreads();
+  if (wave < p.r) gate_run(0, ga, gb, gal, gdt);   // visible after the next barrier
   // q_hat rows and k_hat^T as bf16 (hi, lo) fragments
   {
     const size_t gk = g * p.Hk + m;
@@ -586,42 +612,39 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       dst[i * LDL + 16 * J + li] = r[e] * ra[i] * rj;
     }
   }
-  __syncthreads();  // the q tile is free from here on (reused as A, Tm, then v^T)
+  __syncthreads();  // the q tile is free from here on (reused as A and Tm)
 
   float* sA = sR1;
   float* sT = sR1 + kL * LDL;
-  float* sVt = sR1;
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = m * p.r + hh;
     const size_t gh = g * p.Hv + h;
-    if (wave == 0) {
-      const float av = hh == 0 ? a_in[0] : hh == 1 ? a_in[1] : hh == 2 ? a_in[2] : a_in[3];
-      const float bb = hh == 0 ? b_in[0] : hh == 1 ? b_in[1] : hh == 2 ? b_in[2] : b_in[3];
-      const float al = hh == 0 ? alog[0] : hh == 1 ? alog[1] : hh == 2 ? alog[2] : alog[3];
-      const float db = hh == 0 ? dtb[0] : hh == 1 ? dtb[1] : hh == 2 ? dtb[2] : dtb[3];
-      float gv = 0.f, bv = 0.f;
-      if (lane < nc) gates(al, db, av, bb, gv, bv);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(gv, off, 64);
-        if (lane >= off) gv += y;
+    if (hh > 0 && (hh & 3) == 0) {   // next group of four V-heads
+      if (wave < p.r - hh) {
+        gate_in(hh, ga, gb, gal, gdt);
+        gate_run(hh, ga, gb, gal, gdt);
       }
-      sGam[lane] = gv;
-      sBeta[lane] = bv;
-      sSc[lane] = bv * expf(gv) * sRk[lane];   // W row factor, k's l2 norm folded in
-      p.s.gam[gh * kL + lane] = gv;
+      __syncthreads();
     }
-    __syncthreads();
+    const float* gam = sGam[hh & 3];
+    const float* beta = sBeta[hh & 3];
+    const float* sc = sSc[hh & 3];
+    // v of this head: its loads are in flight while A and P are formed
+    constexpr int VV = 16 / sizeof(Act), VG = D / VV, VTPT = kL * VG / kNT;
+    static_assert(kNT % VG == 0 && VTPT >= 1, "v conv split");
+    const int vgrp = tid % VG, vi_off = (tid / VG) * VTPT;
+    ConvTile<Act, K, VTPT> vct;
+    vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
     // A (for the inverse; only its lower triangle is read) and P (written
     // out as fragments), sharing one decay e^{gamma_i - gamma_j} per element
     for (int u = tid; u < kL * (kL / 8); u += kNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
-      const float gi = sGam[i], bi = sBeta[i];
+      const float gi = gam[i], bi = beta[i];
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        const float dec = j <= i ? __expf(gi - sGam[j]) : 0.f;
+        const float dec = j <= i ? __expf(gi - gam[j]) : 0.f;
         sA[i * LDL + j] = j < i ? bi * dec * sG[i * LDL + j] : 0.f;
         v[e] = dec * sQK[i * LDL + j];
       }
@@ -630,6 +653,14 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       const size_t at = frag_at(gh, kL, kL, i, j0);
       *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
       *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;
+    }
+    {  // v^T, written transposed
+      float out[VTPT][VV];
+      vct.finish(nc, vi_off, out);
+#pragma unroll
+      for (int v = 0; v < VV; ++v)
+#pragma unroll
+        for (int t = 0; t < VTPT; ++t) sVt[(vgrp * VV + v) * LDL + vi_off + t] = out[t][v];
     }
     __syncthreads();
     unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTm[0][0]), tid);
@@ -643,18 +674,6 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       split8(v, h8, l8);
       *reinterpret_cast<bf16x8*>(&sTm[0][i * LDH + j0]) = h8;
       *reinterpret_cast<bf16x8*>(&sTm[1][i * LDH + j0]) = l8;
-    }
-    __syncthreads();  // A and Tm (f32) are dead: v^T goes in their place
-    {  // thread = (16-byte channel run, run of tokens), written transposed
-      constexpr int V = 16 / sizeof(Act), G = D / V, TPT = kL * G / kNT;
-      static_assert(kNT % G == 0 && TPT >= 1, "v conv split");
-      const int grp = tid % G, i_off = (tid / G) * TPT;
-      float out[TPT][V];
-      conv_tile<Act, K, TPT>(p, si, t0, nc, i_off, 2 * p.Hk * D + h * D + grp * V, out);
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-#pragma unroll
-        for (int t = 0; t < TPT; ++t) sVt[(grp * V + v) * LDL + i_off + t] = out[t][v];
     }
     __syncthreads();
     // Tm rows 16 tb + li for both products: as the A operand of U and as the
@@ -676,8 +695,8 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int k = 32 * ks + 8 * lk + e;
-          kv[e] = sSc[k] * sK[k * LDD + d];
-          vv[e] = sBeta[k] * sVt[d * LDL + k];
+          kv[e] = sc[k] * sK[k * LDD + d];
+          vv[e] = beta[k] * sVt[d * LDL + k];
         }
         split8(kv, kh[ks], kl[ks]);
         split8(vv, vh[ks], vl[ks]);

@@ -100,6 +100,15 @@ def test_prefill_conv_widths(K):
     _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"K={K}")
 
 
+@pytest.mark.parametrize("Hk,Hv", [(1, 8), (2, 6), (4, 4)])
+def test_prefill_gqa_ratios(Hk, Hv):
+    """8, 3 and 1 V-heads per K-head (the prep kernel forms the gates in
+    groups of up to four V-heads)."""
+    s = wl.Shape(Hk, Hv, 32, 32, 4, "bf16")
+    w, rec, conv, cu, d = _packed(500 + Hv, s, [97, 40], 3)
+    _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"Hk={Hk} Hv={Hv}")
+
+
 def test_prefill_slow_decay_long_carry():
     """Slow decay (e^g ~ 0.98..0.998) so the state carries across many chunks."""
     s = wl.RANK_LOCAL
