@@ -55,6 +55,12 @@ def parse():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 512 MiB device copy kernel (the reference "
                          "for scaling the HBM byte counters of a profiler run)")
+    ap.add_argument("--calibration-gemm", action="store_true",
+                    help="also run a bf16 8192^3 library GEMM (a reference reading for "
+                         "the MFMA-busy counters of a profiler run)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the two prefill workloads and print their figures "
+                         "(for profiler runs of the prefill kernels)")
     return ap.parse_args()
 
 
@@ -183,24 +189,25 @@ def bench_decode(args):
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_step_b16_hk8_hv16_d128_traffic.md")
 TRAFFIC_SOURCES = ("linear_attention_causal_amd/csrc/decode.hip",
                    "linear_attention_causal_amd/csrc/gdn_device.hpp")
+MFMA_RECORD = os.path.join(ROOT, "profiles", "prefill_t4096_varlen8_d128.md")
+MFMA_SOURCES = ("linear_attention_causal_amd/csrc/prefill.hip",
+                "linear_attention_causal_amd/csrc/gdn_device.hpp")
 
 
-def kernel_source_digest():
+def kernel_source_digest(sources=TRAFFIC_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per decode launch from the committed counter record (FETCH_SIZE
-    and WRITE_SIZE passes, each scaled by the same counter's reading on a plain
-    copy of known size), or None when there is no record or the kernel source
-    has changed since it was taken."""
+def read_record(path, sources):
+    """The `record:` line of a committed profiler summary, or None when there is
+    none or the kernel sources have changed since the counters were taken."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(path) as f:
             text = f.read()
     except OSError:
         return None
@@ -208,9 +215,23 @@ def recorded_traffic():
     for ln in text.splitlines():
         if ln.startswith("record: "):
             rec = json.loads(ln[len("record: "):])
-    if not rec or rec.get("source_sha256") != kernel_source_digest():
+    if not rec or rec.get("source_sha256") != kernel_source_digest(sources):
         return None
     return rec
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter record (FETCH_SIZE
+    and WRITE_SIZE passes, each scaled by the same counter's reading on a plain
+    copy of known size)."""
+    return read_record(TRAFFIC_RECORD, TRAFFIC_SOURCES)
+
+
+def recorded_mfma_util(workload):
+    """MFMA-pipe utilisation (percent, kernel-time weighted over a prefill call)
+    from the committed counter record, or None."""
+    rec = read_record(MFMA_RECORD, MFMA_SOURCES)
+    return rec["mfma_pipe_util_pct"].get(workload) if rec else None
 
 
 def calibration_copy(nbytes=512 << 20, reps=4):
@@ -223,6 +244,18 @@ def calibration_copy(nbytes=512 << 20, reps=4):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     log(f"[bench] calibration copy: {nbytes} bytes read + {nbytes} written per launch, {reps} launches")
+
+
+def calibration_gemm(n=8192, reps=4):
+    """A bf16 n^3 matmul through the library GEMM: a kernel that keeps the MFMA
+    pipes busy, to read the MFMA-busy counters against."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(reps):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration gemm: bf16 {n}^3, {reps} launches")
 
 
 # ------------------------------------------------------------------ prefill
@@ -281,6 +314,10 @@ def bench_prefill(work, iters, replicas):
             "algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
             "mfma_frac_of_bf16_peak": flops / (ms * 1e-3) / BF16_PEAK,
             "mfma_frac_of_f32_peak": flops / (ms * 1e-3) / F32_MFMA_PEAK,
+            "mfma_pipe_util_pct": recorded_mfma_util(work.name),
+            "mfma_pipe_util_source": "rocprofv3 MfmaUtil, kernel-time weighted over the call "
+                                     "(committed prefill profile record; null once the "
+                                     "kernels change)",
             "mfma_dtype": "bf16 x3 (hi/lo split operands, f32 accumulate)", "kernels": 4}
 
 
@@ -325,9 +362,17 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
     stream = torch.cuda.current_stream()
     pools = [L["pool"] for L in Ls]
     compact_ms = []
+    # device-resident slot index: the captured step reads it, a retire event
+    # rewrites it in place
+    slot_d = _t(live, torch.int32)
 
-    def run(nsteps, live):
-        slot_d = _t(live, torch.int32)
+    def layer_pass(st):
+        for L in Ls:
+            gdn.gdn_decode_step(geom, L["w"], L["pool"], slot_d, x, z, a, b, y, stream=st)
+
+    graph = None
+
+    def run(nsteps, live, use_graph):
         for t in range(nsteps):
             if t > 0 and t % 16 == 0:
                 keep, new_slots, src, dst = wl.retire_plan(rng, live, P)
@@ -341,25 +386,43 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
                 admitted = np.arange(len(new_slots), len(new_slots) + (len(live) - len(new_slots)),
                                      dtype=np.int32)
                 live = np.concatenate([new_slots, admitted]).astype(np.int32)
-                slot_d = _t(live, torch.int32)
-            for L in Ls:
-                gdn.gdn_decode_step(geom, L["w"], L["pool"], slot_d, x, z, a, b, y,
-                                    stream=stream)
+                slot_d.copy_(torch.from_numpy(live))
+            if use_graph:
+                graph.replay()
+            else:
+                layer_pass(stream)
         return live
 
-    live = run(2, live)
+    live = run(2, live, False)
     torch.cuda.synchronize()
     compact_ms.clear()
     t0 = time.perf_counter()
-    run(steps, live)
+    live = run(steps, live, False)
+    torch.cuda.synchronize()
+    eager_dt = time.perf_counter() - t0
+    compact_ms.clear()
+    # one HIP graph per step: the 48 layer launches captured once
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            layer_pass(side)
+    stream.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps, live, True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     cms = [a_.elapsed_time(b_) for a_, b_, _ in compact_ms]
     moved = [n for _, _, n in compact_ms]
     per_step = layers * step_bytes(geom, B, 2)
     return {"workload": f"decode_b{B}_hk16_hv32_d128_p{P}_x{layers}layers",
+            "launch": "HIP graph of the 48 layer launches per step, replayed",
             "tokens_per_s": B * steps / dt, "ms_per_step": dt * 1e3 / steps,
             "hbm_frac_algorithmic": per_step * steps / dt / HBM_PEAK,
+            "eager_tokens_per_s": B * steps / eager_dt,
             "compaction_events": len(cms), "compaction_ms": cms, "compaction_pairs": moved,
             "steps": steps}
 
@@ -412,10 +475,21 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        import workloads as wl
+        if args.calibration_gemm:
+            calibration_gemm()
+        out = [bench_prefill(wl.prefill_single(seed=0), iters=10, replicas=6)]
+        torch.cuda.empty_cache()
+        out.append(bench_prefill(wl.prefill_varlen(seed=0), iters=5, replicas=1))
+        print(json.dumps({"prefill": out}), flush=True)
+        return
     log("[bench] decode headline")
     dec = bench_decode(args)
     if args.calibration_copy:
         calibration_copy()
+    if args.calibration_gemm:
+        calibration_gemm()
     line = {
         "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": dec["steps"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
