@@ -764,10 +764,18 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][DVT * LR];   // V'
   __shared__ __attribute__((aligned(16))) __bf16 sD[2][DVT * LR];   // e^{gamma_L - gamma} V'
 
-  const int n = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * DVT;
+  // Workgroup id -> (sequence, V-head, column tile): the r * tiles
+  // workgroups of one (sequence, K-head) get ids 8 apart, so they land on one
+  // XCD and are dispatched together; the chunk operands of the K-head and of
+  // its V-heads then come from HBM once per XCD L2 rather than once per tile.
+  const int tiles = D / DVT, per = p.r * tiles;
+  const int grp = blockIdx.x / (8 * per), rem = blockIdx.x - grp * 8 * per;
+  const int unit = grp * 8 + (rem & 7), k = rem >> 3;
+  if (unit >= p.N * p.Hk) return;
+  const int n = unit / p.Hk, m = unit - n * p.Hk;
+  const int h = m * p.r + k / tiles, col0 = (k % tiles) * DVT;
   const SeqInfo si = seq_info(p, n);
   if (si.slot < 0) return;
-  const int m = h / p.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
   const bool rec = wave < 4;                   // recurrence wave
@@ -965,7 +973,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   // first V-head.  No other workgroup reads these channels of the window
   // (the prep kernel, an earlier launch, read all of them).
   {
-    const bool qk = blockIdx.z == 0 && h % p.r == 0;
+    const bool qk = col0 == 0 && h % p.r == 0;
     const int nch = DVT + (qk ? 2 * D : 0);
     const int vbase = 2 * p.Hk * D + h * D + col0;
     void* win = static_cast<char*>(p.conv) + (size_t)si.slot * K * p.C * io::bytes;
@@ -1047,9 +1055,10 @@ static int state_col_blocks(int N, int Hv, int D) {
 
 template <typename Act, int D, int K, int NCB>
 static void launch_state(const PrefillParams& p, hipStream_t st) {
-  // tiles of one (sequence, head) are N * Hv workgroups apart: with N * Hv a
-  // multiple of 8 they share an XCD and its L2 for the chunk operands
-  prefill_state_kernel<Act, D, K, NCB><<<dim3(p.N, p.Hv, D / (16 * NCB)), kSNT, 0, st>>>(p);
+  // groups of 8 (sequence, K-head) units, each unit r * tiles workgroups
+  const long long units = (long long)p.N * p.Hk, per = (long long)p.r * (D / (16 * NCB));
+  const long long groups = (units + 7) / 8;
+  prefill_state_kernel<Act, D, K, NCB><<<dim3((unsigned)(groups * 8 * per)), kSNT, 0, st>>>(p);
 }
 
 template <typename Act, int D, int K>
