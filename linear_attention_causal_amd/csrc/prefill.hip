@@ -993,12 +993,16 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------------ 3. norm
 
-// 256 threads = 8 token rows x 32 lanes; a lane owns D/32 consecutive values.
+// 256 threads = 8 token rows x 32 lanes; a lane owns D/32 consecutive values
+// of each of the chunk's rows r, r + 8, ...  Every load of the chunk (the
+// pre-norm output and z, rows clamped to the chunk so no load is
+// conditional) is requested before any arithmetic.
 template <typename Act, int D>
 __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int VPL = D / 32;      // values per lane
   constexpr int ROWS = kNT / 32;   // rows per pass
+  constexpr int NP = kL / ROWS;    // passes
   const int c = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
@@ -1007,37 +1011,65 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   const long long tok0 = si.begin + t0;
   const int tid = threadIdx.x, sub = tid & 31, rr = tid >> 5;
   const int d0 = sub * VPL;
+  if (si.slot < 0) {  // padding sequence: zero outputs
+    for (int pass = 0; pass < NP; ++pass) {
+      const int i = pass * ROWS + rr;
+      if (i < nc)
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+          const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0 + k;
+          io::store(p.y, o, 0.f);
+          p.obuf[o] = 0.f;
+        }
+    }
+    return;
+  }
+  float ov[NP][VPL], zv[NP][VPL];
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    const int i = min(pass * ROWS + rr, nc - 1);
+    const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0;
+    if constexpr (VPL == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.obuf + o);
+      const f32x4 z = io::load4(p.z, o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ov[pass][k] = v[k];
+        zv[pass][k] = z[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        ov[pass][k] = p.obuf[o + k];
+        zv[pass][k] = io::load(p.z, o + k);
+      }
+    }
+  }
   float nw[VPL];
 #pragma unroll
   for (int k = 0; k < VPL; ++k) nw[k] = p.norm_w[d0 + k];
 #pragma unroll
-  for (int pass = 0; pass < kL / ROWS; ++pass) {
+  for (int pass = 0; pass < NP; ++pass) {
     const int i = pass * ROWS + rr;
-    const bool ok = i < nc;
-    const size_t o = ((size_t)(tok0 + (ok ? i : 0)) * p.Hv + h) * D + d0;
-    if (si.slot < 0) {  // padding sequence: zero outputs
-      if (ok)
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-          io::store(p.y, o + k, 0.f);
-          p.obuf[o + k] = 0.f;
-        }
-      continue;
-    }
-    float ov[VPL], zv[VPL];
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      ov[k] = ok ? p.obuf[o + k] : 0.f;
-      zv[k] = ok ? io::load(p.z, o + k) : 0.f;
-      ss = fmaf(ov[k], ov[k], ss);
-    }
+    for (int k = 0; k < VPL; ++k) ss = fmaf(ov[pass][k], ov[pass][k], ss);
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
-    if (ok)
+    if (i < nc) {
+      const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0;
+      if constexpr (VPL == 4) {
+        f32x4 yv;
 #pragma unroll
-      for (int k = 0; k < VPL; ++k) io::store(p.y, o + k, nw[k] * ov[k] * inv * silu(zv[k]));
+        for (int k = 0; k < 4; ++k) yv[k] = nw[k] * ov[pass][k] * inv * silu_fast(zv[pass][k]);
+        io::store4(p.y, o, yv);
+      } else {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+          io::store(p.y, o + k, nw[k] * ov[pass][k] * inv * silu_fast(zv[pass][k]));
+      }
+    }
   }
 }
 
