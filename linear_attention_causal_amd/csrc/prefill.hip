@@ -37,8 +37,9 @@
 namespace gdn {
 
 constexpr int kL = 64;        // chunk length
-constexpr int kNT = 256;      // threads per workgroup (4 waves)
-constexpr int kNW = kNT / 64;
+constexpr int kNT = 256;      // threads per workgroup of the norm kernel (4 waves)
+constexpr int kPNT = 512;     // threads per workgroup of the prep kernel (8 waves)
+constexpr int kPNW = kPNT / 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -415,15 +416,15 @@ __device__ __forceinline__ f32x4 mm16(const float* A, int lda, const float* B, i
 
 // Tm = (I + A)^{-1} for strictly lower-triangular A [64][LDL] in LDS, blocked
 // by 16: the four diagonal blocks by forward substitution (one lane per
-// column), then wave jb walks down column block jb,
+// column), then wave jb < 4 walks down column block jb,
 //   T_ib,jb = -T_ib,ib sum_{jb <= kb < ib} A_ib,kb T_kb,jb,   ib = jb+1 .. 3,
-// reading only its own earlier blocks and the diagonal ones.  Called by all
-// four waves; ends with the lower blocks of the result in sT (the strictly
+// reading only its own earlier blocks and the diagonal ones.  Called by every
+// wave of the workgroup; ends with the lower blocks of the result in sT (the strictly
 // upper blocks of sT are left as they are: the caller treats them as zero).
 template <int LDL>
 __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int tid) {
   const int lane = tid & 63, wave = wave_id();
-  if (lane < 16) {
+  if (wave < 4 && lane < 16) {
     // column sweeps: once t_j is final, remove its term from every later row,
     // so the dependency chain is 15 steps long
     const int b0 = 16 * wave, c = lane;
@@ -439,8 +440,8 @@ __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int ti
   }
   __syncthreads();
   const int li = lane & 15, lk = lane >> 4;
-  const int jb = wave;
-  float* M = sM + wave * 16 * 17;   // this wave's 16 x 16 staging tile
+  const int jb = wave;              // waves 4 and up have no column block
+  float* M = sM + (wave & 3) * 16 * 17;   // this wave's 16 x 16 staging tile
   for (int ib = jb + 1; ib < 4; ++ib) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kb = jb; kb < ib; ++kb)
@@ -464,13 +465,13 @@ __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int ti
 //   W = Tm diag(beta e^gamma) K,  U = Tm diag(beta) V
 // so that the sequential pass only has V' = U - W S and the state update left.
 template <typename Act, int D, int K>
-__global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPNT) void prefill_prep_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NKS = D / 32, NDB = D / 16;
   constexpr int LDH = kL + 8;   // bf16 row length of the split Tm
   constexpr int R1A = kL * LDD, R1B = 2 * kL * LDL;
   constexpr int R1 = R1A > R1B ? R1A : R1B;
-  static_assert(kNW * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the Tm tiles");
+  static_assert(4 * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the Tm tiles");
   __shared__ __attribute__((aligned(16))) float sR1[R1];        // q_hat; then A | Tm
   __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k_hat rows
   __shared__ float sG[kL * LDL];                                // K K^T
@@ -516,11 +517,12 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     p.s.gam[(g * p.Hv + h) * kL + lane] = gv;
   };
   float ga = 0.f, gb = 0.f, gal = 0.f, gdt = 0.f;
-  if (wave < p.r) gate_in(0, ga, gb, gal, gdt);
+  const int gate_waves = min(p.r, 4);   // one per gate slot
+  if (wave < gate_waves) gate_in(0, ga, gb, gal, gdt);
   // conv + SiLU of q_m and k_m: thread = (16-byte channel run, run of tokens)
   {
-    constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kNT;
-    static_assert(kNT % G == 0 && TPT >= 1, "q/k conv split");
+    constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kPNT;
+    static_assert(kPNT % G == 0 && TPT >= 1, "q/k conv split");
     const int grp = tid % G, i_off = (tid / G) * TPT;
     const int c0 = grp * V;                      // 0 .. 2D-1: q then k
     const int ch = c0 < D ? m * D + c0 : (p.Hk + m) * D + (c0 - D);
@@ -538,19 +540,19 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
   }
   __syncthreads();
   // l2 norms as per-row factors (q's includes the 1/sqrt(dk) scale), applied
-  // where the rows are used: four lanes per row
+  // where the rows are used: PARTS lanes per row
   {
-    constexpr int QD = D / 4;
-    const int i = tid >> 2, part = tid & 3;
+    constexpr int PARTS = kPNT / kL, QD = D / PARTS;
+    const int i = tid / PARTS, part = tid % PARTS;
     float sq = 0.f, sk = 0.f;
-#pragma unroll 8
+#pragma unroll
     for (int d = part * QD; d < (part + 1) * QD; ++d) {
       const float qv = sQ[i * LDD + d], kv = sK[i * LDD + d];
       sq = fmaf(qv, qv, sq);
       sk = fmaf(kv, kv, sk);
     }
 #pragma unroll
-    for (int off = 1; off < 4; off <<= 1) {
+    for (int off = 1; off < PARTS; off <<= 1) {
       sq += __shfl_xor(sq, off, 64);
       sk += __shfl_xor(sk, off, 64);
     }
@@ -560,11 +562,11 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     }
   }
   __syncthreads();
-  if (wave < p.r) gate_run(0, ga, gb, gal, gdt);   // visible after the next barrier
+  if (wave < gate_waves) gate_run(0, ga, gb, gal, gdt);   // visible after the next barrier
   // q_hat rows and k_hat^T as bf16 (hi, lo) fragments
   {
     const size_t gk = g * p.Hk + m;
-    for (int u = tid; u < kL * (D / 8); u += kNT) {
+    for (int u = tid; u < kL * (D / 8); u += kPNT) {
       const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
       float v[8];
 #pragma unroll
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
       *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;
     }
-    for (int u = tid; u < D * (kL / 8); u += kNT) {
+    for (int u = tid; u < D * (kL / 8); u += kPNT) {
       const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
       float v[8];
 #pragma unroll
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     }
   }
   // K K^T and Q K^T, lower block triangle, 3-pass bf16
-  for (int t = wave; t < 2 * NTL * (NTL + 1) / 2; t += kNW) {
+  for (int t = wave; t < 2 * NTL * (NTL + 1) / 2; t += kPNW) {
     const bool isG = t < NTL * (NTL + 1) / 2;
     int I = 0, rem = isG ? t : t - NTL * (NTL + 1) / 2;
     while (rem > I) { rem -= I + 1; ++I; }
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     const int h = m * p.r + hh;
     const size_t gh = g * p.Hv + h;
     if (hh > 0 && (hh & 3) == 0) {   // next group of four V-heads
-      if (wave < p.r - hh) {
+      if (wave < min(p.r - hh, 4)) {
         gate_in(hh, ga, gb, gal, gdt);
         gate_run(hh, ga, gb, gal, gdt);
       }
@@ -630,14 +632,17 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     const float* beta = sBeta[hh & 3];
     const float* sc = sSc[hh & 3];
     // v of this head: its loads are in flight while A and P are formed
-    constexpr int VV = 16 / sizeof(Act), VG = D / VV, VTPT = kL * VG / kNT;
-    static_assert(kNT % VG == 0 && VTPT >= 1, "v conv split");
+    // (kL * VG / VTPT threads take part: whole waves, the rest skip it)
+    constexpr int VV = 16 / sizeof(Act), VG = D / VV;
+    constexpr int VTPT = kL * VG >= kPNT ? kL * VG / kPNT : 1;
+    static_assert(kPNT % VG == 0 && (kL * VG / VTPT) % 64 == 0, "v conv split");
+    const bool vact = tid < kL * VG / VTPT;
     const int vgrp = tid % VG, vi_off = (tid / VG) * VTPT;
     ConvTile<Act, K, VTPT> vct;
-    vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
+    if (vact) vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
     // A (for the inverse; only its lower triangle is read) and P (written
     // out as fragments), sharing one decay e^{gamma_i - gamma_j} per element
-    for (int u = tid; u < kL * (kL / 8); u += kNT) {
+    for (int u = tid; u < kL * (kL / 8); u += kPNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
       const float gi = gam[i], bi = beta[i];
       float v[8];
@@ -654,7 +659,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
       *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
       *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;
     }
-    {  // v^T, written transposed
+    if (vact) {  // v^T, written transposed
       float out[VTPT][VV];
       vct.finish(nc, vi_off, out);
 #pragma unroll
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
     }
     __syncthreads();
     unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTm[0][0]), tid);
-    for (int u = tid; u < kL * (kL / 8); u += kNT) {
+    for (int u = tid; u < kL * (kL / 8); u += kPNT) {
       const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
       const bool upper = (j0 >> 4) > (i >> 4);   // strictly upper block: zero
       float v[8];
@@ -686,7 +691,7 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillParams p) {
         th[tb][ks] = ld8(&sTm[0][(16 * tb + li) * LDH + 32 * ks + 8 * lk]);
         tl[tb][ks] = ld8(&sTm[1][(16 * tb + li) * LDH + 32 * ks + 8 * lk]);
       }
-    for (int db = wave; db < NDB; db += kNW) {
+    for (int db = wave; db < NDB; db += kPNW) {
       const int d = 16 * db + li;
       bf16x8 kh[2], kl[2], vh[2], vl[2];
 #pragma unroll
@@ -1097,7 +1102,7 @@ template <typename Act, int D, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
   prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
   if (max_chunks > 0)
-    prefill_prep_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
+    prefill_prep_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kPNT, 0, st>>>(p);
   switch (state_col_blocks(p.N, p.Hv, D)) {
     case 1: launch_state<Act, D, K, 1>(p, st); break;
     case 2: launch_state<Act, D, K, 2>(p, st); break;
