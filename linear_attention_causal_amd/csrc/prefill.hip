@@ -649,9 +649,11 @@ __global__ __launch_bounds__(kPNT) void prefill_prep_kernel(PrefillParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
+        // selects, not products with a zero mask: the strictly upper blocks
+        // of sG and sQK are never written and may hold any bits
         const float dec = j <= i ? __expf(gi - gam[j]) : 0.f;
         sA[i * LDL + j] = j < i ? bi * dec * sG[i * LDL + j] : 0.f;
-        v[e] = dec * sQK[i * LDL + j];
+        v[e] = j <= i ? dec * sQK[i * LDL + j] : 0.f;
       }
       bf16x8 h8, l8;
       split8(v, h8, l8);
