@@ -37,9 +37,8 @@
 namespace gdn {
 
 constexpr int kL = 64;        // chunk length
-constexpr int kNT = 256;      // threads per workgroup of the norm kernel (4 waves)
-constexpr int kPNT = 512;     // threads per workgroup of the prep kernel (8 waves)
-constexpr int kPNW = kPNT / 64;
+constexpr int kNT = 256;      // threads per workgroup of the q/k, WY and norm kernels
+constexpr int kNW = kNT / 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -56,13 +55,14 @@ struct PrefillScratch {
   __bf16* w[2];            //         [G][Hv] 64 x D    -Tm diag(beta e^gamma) K
   __bf16* pm[2];           //         [G][Hv] 64 x 64   masked, decayed Q K^T
   float* ut;               // [G][Hv] 64 x D Tm diag(beta) V, accumulator blocks
+  float* gq;               // [G][Hk][2][64][64] K K^T and Q K^T (lower blocks), f32
   float* gam;              // [G][Hv][64] running sum of g
   float* o;                // [T][Hv][D] pre-norm output
 };
 
 static size_t chunk_bound(long long T, long long N) { return (size_t)((T + kL - 1) / kL + N); }
 
-constexpr int kScratchParts = 12;
+constexpr int kScratchParts = 13;
 
 struct ScratchPlan {
   size_t off[kScratchParts];
@@ -79,6 +79,7 @@ static ScratchPlan plan_scratch(const gdn_geometry& g, long long T, long long N)
       G * Hv * kL * D * 2, G * Hv * kL * D * 2,      // w
       G * Hv * kL * kL * 2, G * Hv * kL * kL * 2,    // pm
       G * Hv * D * kL * 4,                           // ut
+      G * Hk * 2 * kL * kL * 4,                      // gq
       G * Hv * kL * 4,                               // gam
       (size_t)T * Hv * D * 4};                       // o
   ScratchPlan sp;
@@ -107,8 +108,9 @@ static PrefillScratch carve(const gdn_geometry& g, long long T, long long N, voi
     s.pm[k] = reinterpret_cast<__bf16*>(c + sp.off[7 + k]);
   }
   s.ut = reinterpret_cast<float*>(c + sp.off[9]);
-  s.gam = reinterpret_cast<float*>(c + sp.off[10]);
-  s.o = reinterpret_cast<float*>(c + sp.off[11]);
+  s.gq = reinterpret_cast<float*>(c + sp.off[10]);
+  s.gam = reinterpret_cast<float*>(c + sp.off[11]);
+  s.o = reinterpret_cast<float*>(c + sp.off[12]);
   return s;
 }
 
@@ -455,74 +457,38 @@ __device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int ti
   __syncthreads();
 }
 
-// One workgroup per (chunk, sequence, K-head).  Everything here depends on
-// the chunk's own tokens only (WY form of the chunk, Gated DeltaNet paper,
-// chunkwise training section):
-//   q_hat, k_hat^T                          per K-head, as bf16 hi/lo rows
-//   gamma = running sum of g, beta          per V-head
+// Both prep kernels depend on a chunk's own tokens only (WY form of the
+// chunk, Gated DeltaNet paper, chunkwise training section):
+//   q_hat, k_hat^T, K K^T, Q K^T            per K-head     (prefill_qk_kernel)
+//   gamma = running sum of g, beta          per V-head     (prefill_wy_kernel)
 //   A = strict_lower(beta_i e^{gamma_i - gamma_j} k_i.k_j), Tm = (I + A)^{-1}
 //   P = lower(e^{gamma_i - gamma_j} q_i.k_j)
 //   W = Tm diag(beta e^gamma) K,  U = Tm diag(beta) V
-// so that the sequential pass only has V' = U - W S and the state update left.
+// so that the sequential pass only has V' = U - W S and the state update
+// left.  Each kernel keeps under 80 KB of LDS so that two workgroups share a
+// CU and hide each other's latencies.
+
+// One workgroup per (chunk, sequence, K-head).
 template <typename Act, int D, int K>
-__global__ __launch_bounds__(kPNT) void prefill_prep_kernel(PrefillParams p) {
-  using io = act_io<Act>;
-  constexpr int LDD = D + 4, LDL = kL + 4, NTL = kL / 16, NKS = D / 32, NDB = D / 16;
-  constexpr int LDH = kL + 8;   // bf16 row length of the split Tm
-  constexpr int R1A = kL * LDD, R1B = 2 * kL * LDL;
-  constexpr int R1 = R1A > R1B ? R1A : R1B;
-  static_assert(4 * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the Tm tiles");
-  __shared__ __attribute__((aligned(16))) float sR1[R1];        // q_hat; then A | Tm
-  __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k_hat rows
-  __shared__ float sG[kL * LDL];                                // K K^T
-  __shared__ float sQK[kL * LDL];                               // Q K^T
-  __shared__ __attribute__((aligned(16))) __bf16 sTm[2][kL * LDH];   // Tm hi, lo
-  __shared__ __attribute__((aligned(16))) float sVt[D * LDL];   // v^T of the current V-head
-  __shared__ float sGam[4][kL], sBeta[4][kL], sSc[4][kL], sRq[kL], sRk[kL];
-  float* sQ = sR1;
+__global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
+  constexpr int LDD = D + 4, NTL = kL / 16, NKS = D / 32;
+  __shared__ __attribute__((aligned(16))) float sQ[kL * LDD];   // q rows (unnormalized)
+  __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k rows (unnormalized)
+  __shared__ float sRq[kL], sRk[kL];
 
   const int c = blockIdx.x, n = blockIdx.y, m = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
   if (si.slot < 0 || t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
-  const long long tok0 = si.begin + t0;
-  const size_t g = (size_t)p.s.chunk_base[n] + c;
+  const size_t gk = ((size_t)p.s.chunk_base[n] + c) * p.Hk + m;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
-  // Gates of the K-head's V-heads m r + hh, four at a time, wave w taking
-  // hh0 + w: running sum gamma, beta, and the W row factor beta e^gamma / |k|
-  // into slot hh & 3.  The first group's inputs are requested up front.
-  const long long gate_tok = tok0 + min(lane, nc - 1);
-  auto gate_in = [&](int hh0, float& a_in, float& b_in, float& alog, float& dtb) {
-    const int h = m * p.r + hh0 + wave;
-    a_in = io::load(p.a, (size_t)gate_tok * p.Hv + h);
-    b_in = io::load(p.b, (size_t)gate_tok * p.Hv + h);
-    alog = p.A_log[h];
-    dtb = p.dt_bias[h];
-  };
-  auto gate_run = [&](int hh0, float a_in, float b_in, float alog, float dtb) {
-    const int hh = hh0 + wave, h = m * p.r + hh;
-    float gv = 0.f, bv = 0.f;
-    if (lane < nc) gates(alog, dtb, a_in, b_in, gv, bv);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(gv, off, 64);
-      if (lane >= off) gv += y;
-    }
-    sGam[hh & 3][lane] = gv;
-    sBeta[hh & 3][lane] = bv;
-    sSc[hh & 3][lane] = bv * expf(gv) * sRk[lane];
-    p.s.gam[(g * p.Hv + h) * kL + lane] = gv;
-  };
-  float ga = 0.f, gb = 0.f, gal = 0.f, gdt = 0.f;
-  const int gate_waves = min(p.r, 4);   // one per gate slot
-  if (wave < gate_waves) gate_in(0, ga, gb, gal, gdt);
   // conv + SiLU of q_m and k_m: thread = (16-byte channel run, run of tokens)
   {
-    constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kPNT;
-    static_assert(kPNT % G == 0 && TPT >= 1, "q/k conv split");
+    constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kNT;
+    static_assert(kNT % G == 0 && TPT >= 1, "q/k conv split");
     const int grp = tid % G, i_off = (tid / G) * TPT;
     const int c0 = grp * V;                      // 0 .. 2D-1: q then k
     const int ch = c0 < D ? m * D + c0 : (p.Hk + m) * D + (c0 - D);
@@ -542,7 +508,7 @@ __global__ __launch_bounds__(kPNT) void prefill_prep_kernel(PrefillParams p) {
   // l2 norms as per-row factors (q's includes the 1/sqrt(dk) scale), applied
   // where the rows are used: PARTS lanes per row
   {
-    constexpr int PARTS = kPNT / kL, QD = D / PARTS;
+    constexpr int PARTS = kNT / kL, QD = D / PARTS;
     const int i = tid / PARTS, part = tid % PARTS;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -562,35 +528,34 @@ __global__ __launch_bounds__(kPNT) void prefill_prep_kernel(PrefillParams p) {
     }
   }
   __syncthreads();
-  if (wave < gate_waves) gate_run(0, ga, gb, gal, gdt);   // visible after the next barrier
   // q_hat rows and k_hat^T as bf16 (hi, lo) fragments
-  {
-    const size_t gk = g * p.Hk + m;
-    for (int u = tid; u < kL * (D / 8); u += kPNT) {
-      const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
-      float v[8];
+  for (int u = tid; u < kL * (D / 8); u += kNT) {
+    const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
+    float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sQ[i * LDD + d0 + e] * sRq[i];
-      bf16x8 h, l;
-      split8(v, h, l);
-      const size_t at = frag_at(gk, kL, D, i, d0);
-      *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
-      *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;
-    }
-    for (int u = tid; u < D * (kL / 8); u += kPNT) {
-      const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d] * sRk[i0 + e];
-      bf16x8 h, l;
-      split8(v, h, l);
-      const size_t at = frag_at(gk, D, kL, d, i0);
-      *reinterpret_cast<bf16x8*>(p.s.kt[0] + at) = h;
-      *reinterpret_cast<bf16x8*>(p.s.kt[1] + at) = l;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = sQ[i * LDD + d0 + e] * sRq[i];
+    bf16x8 h, l;
+    split8(v, h, l);
+    const size_t at = frag_at(gk, kL, D, i, d0);
+    *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
+    *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;
   }
-  // K K^T and Q K^T, lower block triangle, 3-pass bf16
-  for (int t = wave; t < 2 * NTL * (NTL + 1) / 2; t += kPNW) {
+  for (int u = tid; u < D * (kL / 8); u += kNT) {
+    const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d] * sRk[i0 + e];
+    bf16x8 h, l;
+    split8(v, h, l);
+    const size_t at = frag_at(gk, D, kL, d, i0);
+    *reinterpret_cast<bf16x8*>(p.s.kt[0] + at) = h;
+    *reinterpret_cast<bf16x8*>(p.s.kt[1] + at) = l;
+  }
+  // K K^T and Q K^T, lower block triangle, 3-pass bf16, rows scaled by the
+  // norm factors, out as f32 [64][64] (the strictly upper blocks are not
+  // written; their readers select them away)
+  float* gG = p.s.gq + gk * 2 * kL * kL;
+  for (int t = wave; t < 2 * NTL * (NTL + 1) / 2; t += kNW) {
     const bool isG = t < NTL * (NTL + 1) / 2;
     int I = 0, rem = isG ? t : t - NTL * (NTL + 1) / 2;
     while (rem > I) { rem -= I + 1; ++I; }
@@ -604,130 +569,183 @@ __global__ __launch_bounds__(kPNT) void prefill_prep_kernel(PrefillParams p) {
       split8(sK + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
       mfma3(acc, ah, al, bh, bl);
     }
-    const f32x4 r = fold(acc);   // unnormalized rows: scale by the row factors
-    float* dst = isG ? sG : sQK;
+    const f32x4 r = fold(acc);
+    float* dst = gG + (isG ? 0 : kL * kL);
     const float* ra = isG ? sRk : sRq;
     const float rj = sRk[16 * J + li];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * lk + e;
-      dst[i * LDL + 16 * J + li] = r[e] * ra[i] * rj;
+      dst[i * kL + 16 * J + li] = r[e] * ra[i] * rj;
     }
   }
-  __syncthreads();  // the q tile is free from here on (reused as A and Tm)
+}
 
-  float* sA = sR1;
-  float* sT = sR1 + kL * LDL;
-  for (int hh = 0; hh < p.r; ++hh) {
-    const int h = m * p.r + hh;
-    const size_t gh = g * p.Hv + h;
-    if (hh > 0 && (hh & 3) == 0) {   // next group of four V-heads
-      if (wave < min(p.r - hh, 4)) {
-        gate_in(hh, ga, gb, gal, gdt);
-        gate_run(hh, ga, gb, gal, gdt);
-      }
-      __syncthreads();
+// One workgroup per (chunk, sequence, V-head).  W's row factor moves onto
+// Tm (W^T = K^T (Tm diag(beta e^gamma))^T) so W takes k_hat^T straight from
+// the q/k kernel's fragments and no k tile is kept here.
+template <typename Act, int D, int K>
+__global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
+  using io = act_io<Act>;
+  constexpr int LDL = kL + 4, NTL = kL / 16, NDB = D / 16;
+  constexpr int LDH = kL + 8;   // bf16 row length of the split Tm tiles
+  static_assert(D * LDL <= 2 * kL * LDL, "v^T fits the A | Tm tile");
+  static_assert(4 * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits a split tile");
+  __shared__ __attribute__((aligned(16))) float sAT[2 * kL * LDL];   // A | Tm, then v^T
+  __shared__ __attribute__((aligned(16))) __bf16 sTs[2][kL * LDH];   // Tm diag(beta e^gamma)
+  __shared__ __attribute__((aligned(16))) __bf16 sTb[2][kL * LDH];   // Tm diag(beta)
+  __shared__ float sGam[kL], sBeta[kL], sSc[kL];
+  float* sA = sAT;
+  float* sT = sAT + kL * LDL;
+  float* sVt = sAT;
+
+  const int c = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
+  const SeqInfo si = seq_info(p, n);
+  const int t0 = c * kL;
+  if (si.slot < 0 || t0 >= si.len) return;
+  const int nc = min(kL, si.len - t0);
+  const long long tok0 = si.begin + t0;
+  const size_t g = (size_t)p.s.chunk_base[n] + c;
+  const int m = h / p.r;
+  const size_t gh = g * p.Hv + h, gk = g * p.Hk + m;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int li = lane & 15, lk = lane >> 4;
+
+  // the gate inputs (wave 0) and the v conv inputs are requested first
+  float a_in = 0.f, b_in = 0.f, alog = 0.f, dtb = 0.f;
+  if (wave == 0) {
+    const long long tk = tok0 + min(lane, nc - 1);
+    a_in = io::load(p.a, (size_t)tk * p.Hv + h);
+    b_in = io::load(p.b, (size_t)tk * p.Hv + h);
+    alog = p.A_log[h];
+    dtb = p.dt_bias[h];
+  }
+  // (kL * VG / VTPT threads take part: whole waves, the rest skip it)
+  constexpr int VV = 16 / sizeof(Act), VG = D / VV;
+  constexpr int VTPT = kL * VG >= kNT ? kL * VG / kNT : 1;
+  static_assert(kNT % VG == 0 && (kL * VG / VTPT) % 64 == 0, "v conv split");
+  const bool vact = tid < kL * VG / VTPT;
+  const int vgrp = tid % VG, vi_off = (tid / VG) * VTPT;
+  ConvTile<Act, K, VTPT> vct;
+  if (vact) vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
+  // gates: running sum gamma, beta, and the W row factor beta e^gamma
+  if (wave == 0) {
+    float gv = 0.f, bv = 0.f;
+    if (lane < nc) gates(alog, dtb, a_in, b_in, gv, bv);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(gv, off, 64);
+      if (lane >= off) gv += y;
     }
-    const float* gam = sGam[hh & 3];
-    const float* beta = sBeta[hh & 3];
-    const float* sc = sSc[hh & 3];
-    // v of this head: its loads are in flight while A and P are formed
-    // (kL * VG / VTPT threads take part: whole waves, the rest skip it)
-    constexpr int VV = 16 / sizeof(Act), VG = D / VV;
-    constexpr int VTPT = kL * VG >= kPNT ? kL * VG / kPNT : 1;
-    static_assert(kPNT % VG == 0 && (kL * VG / VTPT) % 64 == 0, "v conv split");
-    const bool vact = tid < kL * VG / VTPT;
-    const int vgrp = tid % VG, vi_off = (tid / VG) * VTPT;
-    ConvTile<Act, K, VTPT> vct;
-    if (vact) vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
-    // A (for the inverse; only its lower triangle is read) and P (written
-    // out as fragments), sharing one decay e^{gamma_i - gamma_j} per element
-    for (int u = tid; u < kL * (kL / 8); u += kPNT) {
-      const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
-      const float gi = gam[i], bi = beta[i];
-      float v[8];
+    sGam[lane] = gv;
+    sBeta[lane] = bv;
+    sSc[lane] = bv * expf(gv);
+    p.s.gam[gh * kL + lane] = gv;
+  }
+  __syncthreads();
+  // A (for the inverse; only its lower triangle is read) and P (written out
+  // as fragments), sharing one decay e^{gamma_i - gamma_j} per element
+  const float* gG = p.s.gq + gk * 2 * kL * kL;
+  const float* gQK = gG + kL * kL;
+  for (int u = tid; u < kL * (kL / 8); u += kNT) {
+    const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+    const f32x4 ga = *reinterpret_cast<const f32x4*>(gG + i * kL + j0);
+    const f32x4 gb = *reinterpret_cast<const f32x4*>(gG + i * kL + j0 + 4);
+    const f32x4 qa = *reinterpret_cast<const f32x4*>(gQK + i * kL + j0);
+    const f32x4 qb = *reinterpret_cast<const f32x4*>(gQK + i * kL + j0 + 4);
+    const float gi = sGam[i], bi = sBeta[i];
+    float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = j0 + e;
-        // selects, not products with a zero mask: the strictly upper blocks
-        // of sG and sQK are never written and may hold any bits
-        const float dec = j <= i ? __expf(gi - gam[j]) : 0.f;
-        sA[i * LDL + j] = j < i ? bi * dec * sG[i * LDL + j] : 0.f;
-        v[e] = j <= i ? dec * sQK[i * LDL + j] : 0.f;
-      }
-      bf16x8 h8, l8;
-      split8(v, h8, l8);
-      const size_t at = frag_at(gh, kL, kL, i, j0);
-      *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
-      *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;
+    for (int e = 0; e < 8; ++e) {
+      // selects, not products with a zero mask: the strictly upper blocks
+      // of K K^T and Q K^T are never written and may hold any bits
+      const int j = j0 + e;
+      const float kk = e < 4 ? ga[e] : gb[e - 4], qk = e < 4 ? qa[e] : qb[e - 4];
+      const float dec = j <= i ? __expf(gi - sGam[j]) : 0.f;
+      sA[i * LDL + j] = j < i ? bi * dec * kk : 0.f;
+      v[e] = j <= i ? dec * qk : 0.f;
     }
-    if (vact) {  // v^T, written transposed
-      float out[VTPT][VV];
-      vct.finish(nc, vi_off, out);
+    bf16x8 h8, l8;
+    split8(v, h8, l8);
+    const size_t at = frag_at(gh, kL, kL, i, j0);
+    *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
+    *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;
+  }
+  float vout[VTPT][VV];
+  if (vact) vct.finish(nc, vi_off, vout);   // held until A and Tm are dead
+  __syncthreads();
+  unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTs[0][0]), tid);
+  // Tm scaled by the W and U row factors, split (strictly upper blocks zero)
+  for (int u = tid; u < kL * (kL / 8); u += kNT) {
+    const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+    const bool upper = (j0 >> 4) > (i >> 4);
+    float vs[8], vb[8];
 #pragma unroll
-      for (int v = 0; v < VV; ++v)
-#pragma unroll
-        for (int t = 0; t < VTPT; ++t) sVt[(vgrp * VV + v) * LDL + vi_off + t] = out[t][v];
+    for (int e = 0; e < 8; ++e) {
+      const float t = upper ? 0.f : sT[i * LDL + j0 + e];
+      vs[e] = t * sSc[j0 + e];
+      vb[e] = t * sBeta[j0 + e];
     }
-    __syncthreads();
-    unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTm[0][0]), tid);
-    for (int u = tid; u < kL * (kL / 8); u += kPNT) {
-      const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
-      const bool upper = (j0 >> 4) > (i >> 4);   // strictly upper block: zero
-      float v[8];
+    bf16x8 h8, l8;
+    split8(vs, h8, l8);
+    *reinterpret_cast<bf16x8*>(&sTs[0][i * LDH + j0]) = h8;
+    *reinterpret_cast<bf16x8*>(&sTs[1][i * LDH + j0]) = l8;
+    split8(vb, h8, l8);
+    *reinterpret_cast<bf16x8*>(&sTb[0][i * LDH + j0]) = h8;
+    *reinterpret_cast<bf16x8*>(&sTb[1][i * LDH + j0]) = l8;
+  }
+  __syncthreads();  // A and Tm (f32) are dead: v^T goes in their place
+  if (vact)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = upper ? 0.f : sT[i * LDL + j0 + e];
-      bf16x8 h8, l8;
-      split8(v, h8, l8);
-      *reinterpret_cast<bf16x8*>(&sTm[0][i * LDH + j0]) = h8;
-      *reinterpret_cast<bf16x8*>(&sTm[1][i * LDH + j0]) = l8;
+    for (int v = 0; v < VV; ++v)
+#pragma unroll
+      for (int t = 0; t < VTPT; ++t) sVt[(vgrp * VV + v) * LDL + vi_off + t] = vout[t][v];
+  __syncthreads();
+  for (int db = wave; db < NDB; db += kNW) {
+    const int d = 16 * db + li;
+    // k_hat^T rows d (A operand of W^T), from the q/k kernel
+    bf16x8 kh[2], kl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const size_t at = frag_lane((gk * NDB + db) * 2 + ks, lane);
+      kh[ks] = ld8(p.s.kt[0] + at);
+      kl[ks] = ld8(p.s.kt[1] + at);
     }
-    __syncthreads();
-    // Tm rows 16 tb + li for both products: as the A operand of U and as the
-    // B operand of W^T (the two lane layouts coincide).
-    bf16x8 th[NTL][2], tl[NTL][2];
+    // v^T rows d, split (B operand of U)
+    bf16x8 vh[2], vl[2];
 #pragma unroll
-    for (int tb = 0; tb < NTL; ++tb)
+    for (int ks = 0; ks < 2; ++ks) {
+      float vv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = sVt[d * LDL + 32 * ks + 8 * lk + e];
+      split8(vv, vh[ks], vl[ks]);
+    }
+#pragma unroll
+    for (int tb = 0; tb < NTL; ++tb) {
+      // rows 16 tb + li of the two scaled Tm: B operand of W^T, A operand of U
+      bf16x8 sh[2], sl[2], bh[2], bl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        th[tb][ks] = ld8(&sTm[0][(16 * tb + li) * LDH + 32 * ks + 8 * lk]);
-        tl[tb][ks] = ld8(&sTm[1][(16 * tb + li) * LDH + 32 * ks + 8 * lk]);
+        const int o = (16 * tb + li) * LDH + 32 * ks + 8 * lk;
+        sh[ks] = ld8(&sTs[0][o]);
+        sl[ks] = ld8(&sTs[1][o]);
+        bh[ks] = ld8(&sTb[0][o]);
+        bl[ks] = ld8(&sTb[1][o]);
       }
-    for (int db = wave; db < NDB; db += kPNW) {
-      const int d = 16 * db + li;
-      bf16x8 kh[2], kl[2], vh[2], vl[2];
+      Acc3 aw = acc3(f32x4{0.f, 0.f, 0.f, 0.f});   // W^T: rows d, columns token
+      Acc3 au = acc3(f32x4{0.f, 0.f, 0.f, 0.f});   // U: rows token, columns d
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float kv[8], vv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 32 * ks + 8 * lk + e;
-          kv[e] = sc[k] * sK[k * LDD + d];
-          vv[e] = beta[k] * sVt[d * LDL + k];
-        }
-        split8(kv, kh[ks], kl[ks]);
-        split8(vv, vh[ks], vl[ks]);
+        mfma3(aw, kh[ks], kl[ks], sh[ks], sl[ks]);
+        mfma3(au, bh[ks], bl[ks], vh[ks], vl[ks]);
       }
-#pragma unroll
-      for (int tb = 0; tb < NTL; ++tb) {
-        // W^T tile: rows d (block db), columns token (block tb)
-        Acc3 aw = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
-        // U tile: rows token (block tb), columns d (block db)
-        Acc3 au = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          mfma3(aw, kh[ks], kl[ks], th[tb][ks], tl[tb][ks]);
-          mfma3(au, th[tb][ks], tl[tb][ks], vh[ks], vl[ks]);
-        }
-        const f32x4 wt = -fold(aw);   // -W[token 16 tb + li][d 16 db + 4 lk + e]
-        const size_t wo = frag_at(gh, kL, D, 16 * tb + li, 16 * db + 4 * lk);
-        store_split4(p.s.w[0] + wo, p.s.w[1] + wo, wt);
-        // U tile in the accumulator layout of the state kernel: block
-        // (d block db, token block tb), lane li + 16 lk
-        *reinterpret_cast<f32x4*>(p.s.ut + (((gh * NDB + db) * NTL + tb) * 64 + lane) * 4) = fold(au);
-      }
+      const f32x4 wt = -fold(aw);   // -W[token 16 tb + li][d 16 db + 4 lk + e]
+      const size_t wo = frag_at(gh, kL, D, 16 * tb + li, 16 * db + 4 * lk);
+      store_split4(p.s.w[0] + wo, p.s.w[1] + wo, wt);
+      // U tile in the accumulator layout of the state kernel: block
+      // (d block db, token block tb), lane li + 16 lk
+      *reinterpret_cast<f32x4*>(p.s.ut + (((gh * NDB + db) * NTL + tb) * 64 + lane) * 4) = fold(au);
     }
-    __syncthreads();
   }
 }
 
@@ -1103,8 +1121,10 @@ static void launch_state(const PrefillParams& p, hipStream_t st) {
 template <typename Act, int D, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
   prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
-  if (max_chunks > 0)
-    prefill_prep_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kPNT, 0, st>>>(p);
+  if (max_chunks > 0) {
+    prefill_qk_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
+    prefill_wy_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
+  }
   switch (state_col_blocks(p.N, p.Hv, D)) {
     case 1: launch_state<Act, D, K, 1>(p, st); break;
     case 2: launch_state<Act, D, K, 2>(p, st); break;
