@@ -611,7 +611,22 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
-  // the gate inputs (wave 0) and the v conv inputs are requested first
+  // K K^T and Q K^T rows of this thread's A/P runs, the gate inputs (wave 0)
+  // and the v conv inputs are all requested first
+  constexpr int APR = kL * (kL / 8) / kNT;   // A/P runs per thread
+  static_assert(kL * (kL / 8) % kNT == 0, "A/P split");
+  const float* gG = p.s.gq + gk * 2 * kL * kL;
+  const float* gQK = gG + kL * kL;
+  f32x4 kkr[APR][2], qkr[APR][2];
+#pragma unroll
+  for (int q = 0; q < APR; ++q) {
+    const int u = tid + q * kNT, i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      kkr[q][hf] = *reinterpret_cast<const f32x4*>(gG + i * kL + j0 + 4 * hf);
+      qkr[q][hf] = *reinterpret_cast<const f32x4*>(gQK + i * kL + j0 + 4 * hf);
+    }
+  }
   float a_in = 0.f, b_in = 0.f, alog = 0.f, dtb = 0.f;
   if (wave == 0) {
     const long long tk = tok0 + min(lane, nc - 1);
@@ -645,14 +660,9 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
   __syncthreads();
   // A (for the inverse; only its lower triangle is read) and P (written out
   // as fragments), sharing one decay e^{gamma_i - gamma_j} per element
-  const float* gG = p.s.gq + gk * 2 * kL * kL;
-  const float* gQK = gG + kL * kL;
-  for (int u = tid; u < kL * (kL / 8); u += kNT) {
-    const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
-    const f32x4 ga = *reinterpret_cast<const f32x4*>(gG + i * kL + j0);
-    const f32x4 gb = *reinterpret_cast<const f32x4*>(gG + i * kL + j0 + 4);
-    const f32x4 qa = *reinterpret_cast<const f32x4*>(gQK + i * kL + j0);
-    const f32x4 qb = *reinterpret_cast<const f32x4*>(gQK + i * kL + j0 + 4);
+#pragma unroll
+  for (int q = 0; q < APR; ++q) {
+    const int u = tid + q * kNT, i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
     const float gi = sGam[i], bi = sBeta[i];
     float v[8];
 #pragma unroll
@@ -660,7 +670,7 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
       // selects, not products with a zero mask: the strictly upper blocks
       // of K K^T and Q K^T are never written and may hold any bits
       const int j = j0 + e;
-      const float kk = e < 4 ? ga[e] : gb[e - 4], qk = e < 4 ? qa[e] : qb[e - 4];
+      const float kk = kkr[q][e >> 2][e & 3], qk = qkr[q][e >> 2][e & 3];
       const float dec = j <= i ? __expf(gi - sGam[j]) : 0.f;
       sA[i * LDL + j] = j < i ? bi * dec * kk : 0.f;
       v[e] = j <= i ? dec * qk : 0.f;
