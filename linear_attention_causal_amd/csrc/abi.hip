@@ -241,7 +241,8 @@ int gdn_prefill_chunked(const gdn_geometry* geom, const gdn_layer_weights* w,
     if ((reinterpret_cast<uintptr_t>(scratch) & 255u) != 0)
       return fail(GDN_E_ALIGN, "scratch must be 256-byte aligned");
   }
-  return hip_status(gdn::launch_prefill(*geom, *w, *pool, cu_seqlens_dev, max_len, T, slot_idx,
+  return hip_status(gdn::launch_prefill(*geom, *w, *pool, cu_seqlens_dev, cu_seqlens_host,
+                                        max_len, T, slot_idx,
                                         has_init, N, qkv_in, z, a, b, y, o_raw, scratch,
                                         static_cast<hipStream_t>(stream)),
                     "gdn_prefill_chunked launch");

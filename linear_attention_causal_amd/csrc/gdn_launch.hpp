@@ -31,7 +31,7 @@ size_t prefill_scratch_bytes(const gdn_geometry& g, long long total_tokens,
 
 hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
                           const gdn_state_pool& pool, const int32_t* cu_seqlens,
-                          int max_len, long long total_tokens,
+                          const int32_t* cu_seqlens_host, int max_len, long long total_tokens,
                           const int32_t* slot_idx, const uint8_t* has_init, int N,
                           const void* qkv_in, const void* z, const void* a,
                           const void* b, void* y, float* o_raw, void* scratch,

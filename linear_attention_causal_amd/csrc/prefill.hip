@@ -18,18 +18,23 @@
 // are only formed as e^{gamma_i - gamma_j} with j <= i (<= 1).
 //
 // Launches, in stream order:
-//   0. plan   one workgroup: chunk_base[n] = number of chunks before sequence n.
-//   1. prep   (chunk, sequence, K-head), all chunks in parallel: conv + SiLU
-//             of q/k/v, l2norm, K K^T and Q K^T once per K-head; per V-head
-//             the gates, their running sum, Tm (blocked 16 x 16 triangular
-//             inverse), P, W and U.  Operands are written as bf16 (hi, lo)
-//             pairs (U as f32) in the fragment layout of the next kernel.
-//   2. state  (sequence, V-head, 16 dv columns), sequential over the chunks
-//             of a sequence, the dv columns of S split over workgroups (they
-//             evolve independently): V' = U - W S and the state carry on one
-//             half of the waves, O = e^gamma Q S + P V' on the other half, on
-//             3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo + lo*hi with f32
-//             accumulation, about 2^-16 relative), O (pre-norm) to f32.
+//   0. plan   one workgroup: chunk_base[n] = number of chunks before sequence n
+//             (only for batches of more than kInlineSeqs sequences; smaller
+//             ones carry the prefix, taken from the host copy, in the launch).
+//   1. q/k    (chunk, sequence, K-head), all chunks in parallel: conv + SiLU
+//             of q/k, l2 norms, q_hat and k_hat^T fragments, K K^T and Q K^T.
+//   1'. WY    (chunk, sequence, V-head), all chunks in parallel: the gates and
+//             their running sum, A, P, Tm (blocked 16 x 16 triangular
+//             inverse), conv + SiLU of v, W and U.  Operands are written as
+//             bf16 (hi, lo) pairs (U as f32) in the fragment layout of the
+//             next kernel.
+//   2. state  (sequence, V-head, 16 NCB dv columns), sequential over the
+//             chunks of a sequence, the dv columns of S split over
+//             workgroups (they evolve independently): V' = U - W S and the
+//             state carry on one half of the waves, O = e^gamma Q S + P V' on
+//             the other half, on 3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo
+//             + lo*hi with f32 accumulation, about 2^-16 relative), O
+//             (pre-norm) to f32.
 //   3. norm   (chunk, sequence, V-head): gated RMSNorm with SiLU(z) -> y.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -114,6 +119,8 @@ static PrefillScratch carve(const gdn_geometry& g, long long T, long long N, voi
   return s;
 }
 
+constexpr int kInlineSeqs = 64;
+
 struct PrefillParams {
   const void* x;        // [T][C] act
   const void* z;        // [T][Hv][D] act
@@ -132,6 +139,13 @@ struct PrefillParams {
   const float* norm_w;
   PrefillScratch s;
   long long T;
+  size_t G;             // chunk capacity of the scratch
+  // Small batches: sequence bounds and chunk prefix from the validated host
+  // copy of cu_seqlens, passed with the launch (no plan kernel, no device
+  // read of cu_seqlens); larger ones use the device copy and the plan kernel.
+  bool inl;
+  int32_t inl_cu[kInlineSeqs + 1];
+  int32_t inl_cb[kInlineSeqs + 1];
   int N, Hk, Hv, C, num_slots, r;
   float l2eps, rmseps, scale;
 };
@@ -143,10 +157,20 @@ struct SeqInfo {
   bool init;
 };
 
+// First scratch chunk of sequence n.
+__device__ __forceinline__ size_t chunk_base_of(const PrefillParams& p, int n) {
+  return p.inl ? (size_t)p.inl_cb[n] : (size_t)p.s.chunk_base[n];
+}
+
 __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int n) {
   SeqInfo s;
-  long long b = p.cu[n], e = p.cu[n + 1];
+  long long b = p.inl ? p.inl_cu[n] : p.cu[n], e = p.inl ? p.inl_cu[n + 1] : p.cu[n + 1];
   if (b < 0 || e > p.T || e < b) { b = 0; e = 0; }  // inconsistent copy: treat as empty
+  if (!p.inl && e > b &&
+      (size_t)p.s.chunk_base[n] + (size_t)((e - b + kL - 1) / kL) > p.G) {
+    b = 0;  // a device copy of cu_seqlens that disagrees with the host one
+    e = 0;  // would overrun the scratch: treat the sequence as empty
+  }
   s.begin = b;
   s.len = (int)(e - b);
   const int sl = p.slot_idx[n];
@@ -481,7 +505,7 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
   const int t0 = c * kL;
   if (si.slot < 0 || t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
-  const size_t gk = ((size_t)p.s.chunk_base[n] + c) * p.Hk + m;
+  const size_t gk = (chunk_base_of(p, n) + c) * p.Hk + m;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
@@ -605,7 +629,7 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
   if (si.slot < 0 || t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
   const long long tok0 = si.begin + t0;
-  const size_t g = (size_t)p.s.chunk_base[n] + c;
+  const size_t g = chunk_base_of(p, n) + c;
   const int m = h / p.r;
   const size_t gh = g * p.Hv + h, gk = g * p.Hk + m;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -817,7 +841,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   const int w4 = wave & 3;                     // token-row block (and state row block)
   const int i0 = 16 * w4 + 4 * lk;             // first of this lane's four token rows
   float* Sg = p.rec + ((size_t)si.slot * p.Hv + h) * D * D;
-  const size_t cbase = si.len > 0 ? (size_t)p.s.chunk_base[n] : 0;
+  const size_t cbase = si.len > 0 ? chunk_base_of(p, n) : 0;
   const int nchunks = (si.len + kL - 1) / kL;
 
   f32x4 S[RBW][NCB];
@@ -1130,7 +1154,7 @@ static void launch_state(const PrefillParams& p, hipStream_t st) {
 
 template <typename Act, int D, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
-  prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
+  if (!p.inl) prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
   if (max_chunks > 0) {
     prefill_qk_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
     prefill_wy_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
@@ -1168,7 +1192,7 @@ static hipError_t prefill_d(const PrefillParams& p, int D, int K, int mc, hipStr
 
 hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
                           const gdn_state_pool& pool, const int32_t* cu_seqlens,
-                          int max_len, long long total_tokens,
+                          const int32_t* cu_seqlens_host, int max_len, long long total_tokens,
                           const int32_t* slot_idx, const uint8_t* has_init, int N,
                           const void* qkv_in, const void* z, const void* a,
                           const void* b, void* y, float* o_raw, void* scratch,
@@ -1189,6 +1213,16 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
   p.dt_bias = w.dt_bias;
   p.norm_w = w.norm_weight;
   p.s = carve(g, total_tokens, N, scratch);
+  p.G = chunk_bound(total_tokens, N);
+  p.inl = N <= kInlineSeqs;
+  if (p.inl) {
+    int run = 0;
+    for (int n = 0; n <= N; ++n) {
+      p.inl_cu[n] = cu_seqlens_host[n];
+      p.inl_cb[n] = run;
+      if (n < N) run += (cu_seqlens_host[n + 1] - cu_seqlens_host[n] + kL - 1) / kL;
+    }
+  }
   p.obuf = o_raw ? o_raw : p.s.o;
   p.T = total_tokens;
   p.N = N;

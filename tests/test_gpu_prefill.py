@@ -100,6 +100,21 @@ def test_prefill_conv_widths(K):
     _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"K={K}")
 
 
+def test_prefill_many_sequences_device_prefix():
+    """70 packed sequences (more than the launch carries inline, so the chunk
+    prefix is formed on the device), with empty ones, padding and fresh starts."""
+    s = wl.Shape(2, 4, 32, 32, 4, "bf16")
+    rng = np.random.default_rng(600)
+    N, P = 70, 80
+    lens = rng.integers(0, 90, N)
+    lens[[3, 17, 40]] = 0
+    slots = rng.choice(P, N, replace=False).astype(np.int32)
+    slots[[5, 33]] = -1
+    init = (rng.random(N) < 0.7).astype(np.uint8)
+    w, rec, conv, cu, d = _packed(601, s, list(lens), P)
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="70 sequences")
+
+
 @pytest.mark.parametrize("Hk,Hv", [(1, 8), (2, 6), (4, 4)])
 def test_prefill_gqa_ratios(Hk, Hv):
     """8, 3 and 1 V-heads per K-head (the prep kernel forms the gates in
