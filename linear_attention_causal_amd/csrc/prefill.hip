@@ -1154,7 +1154,8 @@ static void launch_state(const PrefillParams& p, hipStream_t st) {
 
 template <typename Act, int D, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
-  if (!p.inl) prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
+  // (with no tokens there are no chunks and the scratch may be absent)
+  if (!p.inl && p.T > 0) prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
   if (max_chunks > 0) {
     prefill_qk_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
     prefill_wy_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);

@@ -115,6 +115,20 @@ def test_prefill_many_sequences_device_prefix():
     _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="70 sequences")
 
 
+@pytest.mark.parametrize("N", [3, 70])
+def test_prefill_all_sequences_empty(N):
+    """No tokens at all (T = 0, no scratch): each slot keeps its state and
+    window, or is reset to zeros for a fresh start; padding untouched."""
+    s = wl.Shape(2, 4, 32, 32, 4, "bf16")
+    rng = np.random.default_rng(700 + N)
+    P = N + 5
+    slots = rng.choice(P, N, replace=False).astype(np.int32)
+    slots[1] = -1
+    init = (rng.random(N) < 0.5).astype(np.uint8)
+    w, rec, conv, cu, d = _packed(701 + N, s, [0] * N, P)
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag=f"{N} empty sequences")
+
+
 @pytest.mark.parametrize("Hk,Hv", [(1, 8), (2, 6), (4, 4)])
 def test_prefill_gqa_ratios(Hk, Hv):
     """8, 3 and 1 V-heads per K-head (the prep kernel forms the gates in
