@@ -645,10 +645,14 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
   for (int q = 0; q < APR; ++q) {
     const int u = tid + q * kNT, i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
+    // runs wholly above the diagonal are never used: they read the row's
+    // first run instead (a line fetched anyway), so the upper half of the
+    // tiles costs no memory traffic
+    const int jr = j0 <= i ? j0 : 0;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      kkr[q][hf] = *reinterpret_cast<const f32x4*>(gG + i * kL + j0 + 4 * hf);
-      qkr[q][hf] = *reinterpret_cast<const f32x4*>(gQK + i * kL + j0 + 4 * hf);
+      kkr[q][hf] = *reinterpret_cast<const f32x4*>(gG + i * kL + jr + 4 * hf);
+      qkr[q][hf] = *reinterpret_cast<const f32x4*>(gQK + i * kL + jr + 4 * hf);
     }
   }
   float a_in = 0.f, b_in = 0.f, alog = 0.f, dtb = 0.f;
