@@ -15,6 +15,10 @@ Also reported on the same JSON line:
   prefill       4096-token single-sequence prefill (Hk=8, Hv=16) and the
                 8-sequence packed varlen prefill (Hk=16, Hv=32): tokens/s and
                 algorithmic MFMA fraction;
+  block         one decode token per row through the whole block (input
+                projections, the layer, out_proj; hidden 2048) at B = 16
+                rank-local and B = 256 full-head, with the library GEMM timed
+                beside the projection kernel;
   serving       B = 256 rows through 48 layers (Hk=16, Hv=32, 320-slot pools)
                 with a retire + compaction event every 16 steps;
   cpu_baseline  the f64 oracle on the host cores, on a bounded sample of the
@@ -58,6 +62,8 @@ def parse():
     ap.add_argument("--calibration-gemm", action="store_true",
                     help="also run a bf16 8192^3 library GEMM (a reference reading for "
                          "the MFMA-busy counters of a profiler run)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only the decode-block legs (projections + layer)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the two prefill workloads and print their figures "
                          "(for profiler runs of the prefill kernels)")
@@ -321,6 +327,133 @@ def bench_prefill(work, iters, replicas):
             "mfma_dtype": "bf16 x3 (hi/lo split operands, f32 accumulate)", "kernels": 4}
 
 
+# ------------------------------------------------------------------ block
+
+
+def _graph_us(fn, R, warm=2, reps=20):
+    """Mean device time (us) of one of R back-to-back calls fn(r), captured
+    once in a HIP graph and replayed, from HIP events on the replay stream."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for r in range(R):          # eager pass first: library workspaces allocated outside
+            fn(r, side)
+        with torch.cuda.graph(graph, stream=side):
+            for r in range(R):
+                fn(r, side)
+    stream.wait_stream(side)
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3 / R
+
+
+def bench_block(B, shape, P, replicas):
+    """One decode token per row through the whole block: the four input
+    projections (one gdn_linear launch), gdn_decode_step, and out_proj (one
+    gdn_linear launch), on `replicas` rotating copies of the weights and pools
+    so that every block streams its weights and state from HBM.  Each part is
+    also timed on its own, and the five projections are timed through the
+    library GEMM (torch.mm on pre-transposed weights) for comparison."""
+    import torch
+
+    import linear_attention_causal_amd as gdn
+    import workloads as wl
+
+    work = wl.decode_block(seed=0, B=B, P=P, s=shape)
+    s, d = work.shape, work.data
+    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                        s.conv_kernel, s.act)
+    bf = torch.bfloat16
+    H = d["hidden"].shape[1]
+    C, Hv, vd = s.channels, s.num_v_heads, s.num_v_heads * s.head_v_dim
+    wd = dict(conv_w=_t(d["weights"]["conv_w"], bf),
+              A_log=_t(d["weights"]["A_log"], torch.float32),
+              dt_bias=_t(d["weights"]["dt_bias"], torch.float32),
+              norm_w=_t(d["weights"]["norm_w"], torch.float32))
+    lw = gdn.LayerWeights(geom, wd["conv_w"], wd["A_log"], wd["dt_bias"], wd["norm_w"])
+    proj0 = {k: _t(v, bf) for k, v in d["proj"].items()}
+    rec0, conv0 = _t(d["rec"], torch.float32), _t(d["conv"], bf)
+    reps = []
+    for r in range(replicas):
+        rec, conv = rec0.clone(), conv0.clone()
+        reps.append(dict(p={k: v.clone() for k, v in proj0.items()}, rec=rec, conv=conv,
+                         pool=gdn.StatePool(geom, rec, conv), h=_t(d["hidden"], bf)))
+    del proj0, rec0, conv0
+    slot = _t(d["slot_idx"], torch.int32)
+    qkv = torch.empty(B, C, device="cuda", dtype=bf)
+    z = torch.empty(B, vd, device="cuda", dtype=bf)
+    bb = torch.empty(B, Hv, device="cuda", dtype=bf)
+    aa = torch.empty(B, Hv, device="cuda", dtype=bf)
+    y = torch.empty(B, vd, device="cuda", dtype=bf)
+    out = torch.empty(B, H, device="cuda", dtype=bf)
+
+    def in_proj(r, st):
+        R = reps[r]
+        gdn.gdn_linear(R["h"], [(R["p"]["qkv"], qkv), (R["p"]["z"], z), (R["p"]["b"], bb),
+                                (R["p"]["a"], aa)], stream=st)
+
+    def core(r, st):
+        gdn.gdn_decode_step(geom, lw, reps[r]["pool"], slot, qkv, z, aa, bb, y, stream=st)
+
+    def out_proj(r, st):
+        gdn.gdn_linear(y, [(reps[r]["p"]["out"], out)], stream=st)
+
+    def block(r, st):
+        in_proj(r, st)
+        core(r, st)
+        out_proj(r, st)
+
+    R = replicas
+    t_block = _graph_us(block, R)
+    t_in = _graph_us(in_proj, R)
+    t_core = _graph_us(core, R)
+    t_out = _graph_us(out_proj, R)
+    # library GEMM on the same weights, pre-transposed to [in][out] (no transposed views)
+    lib_w = [{k: v.t().contiguous() for k, v in R_["p"].items()} for R_ in reps]
+
+    def lib_in(r, st):
+        h = reps[r]["h"]
+        for k, o in (("qkv", qkv), ("z", z), ("b", bb), ("a", aa)):
+            torch.mm(h, lib_w[r][k], out=o)
+
+    def lib_out(r, st):
+        torch.mm(y, lib_w[r]["out"], out=out)
+
+    t_lib_in = _graph_us(lib_in, R)
+    t_lib_out = _graph_us(lib_out, R)
+    n_in = C + vd + 2 * Hv
+    in_bytes = 2 * (n_in * H + B * H + B * n_in)
+    out_bytes = 2 * (H * vd + B * vd + B * H)
+    core_bytes = step_bytes(geom, B, 2)
+    total = in_bytes + core_bytes + out_bytes
+    flops = 2 * B * H * (n_in + vd)
+    return {"workload": work.name, "rows": B, "hidden": H, "num_k_heads": s.num_k_heads,
+            "num_v_heads": Hv, "head_dim": s.head_k_dim, "launches": 3,
+            "us_per_block": t_block, "tokens_per_s": B / (t_block * 1e-6),
+            "block_bytes": total, "block_hbm_frac": total / (t_block * 1e-6) / HBM_PEAK,
+            "in_proj_us": t_in, "in_proj_hbm_frac": in_bytes / (t_in * 1e-6) / HBM_PEAK,
+            "decode_step_us": t_core,
+            "out_proj_us": t_out, "out_proj_hbm_frac": out_bytes / (t_out * 1e-6) / HBM_PEAK,
+            "projection_tflops": flops / ((t_in + t_out) * 1e-6) / 1e12,
+            "library_in_proj_us": t_lib_in, "library_out_proj_us": t_lib_out,
+            "library": "torch.mm (hipBLASLt), four input launches + one output launch",
+            "timing": f"HIP events around graph replays of {R} back-to-back blocks on "
+                      f"{R} weight/pool replicas"}
+
+
 # ------------------------------------------------------------------ serving
 
 
@@ -490,6 +623,13 @@ def main():
         out.append(bench_prefill(wl.prefill_varlen(seed=0), iters=5, replicas=1))
         print(json.dumps({"prefill": out}), flush=True)
         return
+    if args.block_only:
+        import workloads as wl
+        out = [bench_block(16, wl.RANK_LOCAL, 64, args.replicas)]
+        torch.cuda.empty_cache()
+        out.append(bench_block(256, wl.FULL_HEADS, 320, 4))
+        print(json.dumps({"block": out}), flush=True)
+        return
     log("[bench] decode headline")
     dec = bench_decode(args)
     if args.calibration_copy:
@@ -519,6 +659,12 @@ def main():
         pre.append(bench_prefill(wl.prefill_varlen(seed=0), iters=5, replicas=1))
         torch.cuda.empty_cache()
         line["prefill"] = pre
+        log("[bench] decode block b16")
+        line["block"] = [bench_block(16, wl.RANK_LOCAL, 64, args.replicas)]
+        torch.cuda.empty_cache()
+        log("[bench] decode block b256")
+        line["block"].append(bench_block(256, wl.FULL_HEADS, 320, 4))
+        torch.cuda.empty_cache()
         log("[bench] serving 48 layers")
         line["serving"] = bench_serving()
         torch.cuda.empty_cache()

@@ -196,6 +196,31 @@ int gdn_prefill_chunked(const gdn_geometry* geom, const gdn_layer_weights* w,
                         const void* a, const void* b, void* y, float* o_raw,
                         void* scratch, size_t scratch_bytes, void* stream);
 
+/* ------------------------------------------------------------- projections */
+
+/* One weight of gdn_linear: weight [N][K] bf16 row-major (a Linear layer's
+ * weight), 16-byte aligned; out [M][ldy] bf16, ldy >= N. */
+typedef struct {
+  const void* weight;
+  void* out;
+  int32_t N;
+  int32_t ldy;
+} gdn_linear_out;
+
+/* The projections around the layer core (cortex commit 95dc874,
+ * TpQwen3_5GatedDeltaNet bullet: in_proj_qkv, in_proj_z, in_proj_b and
+ * in_proj_a split along the V-heads, out_proj along its input dimension, so
+ * on one GPU each is a plain product with that GPU's slice of the weight):
+ *   outs[i].out[m][n] = sum_k x[m][k] * outs[i].weight[n][k]
+ * for m < M, n < outs[i].N, with bf16 x and weights, f32 accumulation and
+ * the result rounded once to bf16.  x [M][ldx] bf16 device, 16-byte
+ * aligned, ldx >= K, ldx and K multiples of 8.  outs is a HOST array of
+ * 1..4 outputs that all read the same x (one launch for the input
+ * projections of a token).  No output may overlap x, a weight or another
+ * output (GDN_E_OVERLAP).  M == 0 is a no-op. */
+int gdn_linear(const void* x, int32_t M, int32_t K, int32_t ldx,
+               const gdn_linear_out* outs, int32_t count, void* stream);
+
 /* ------------------------------------------------------------- retire */
 
 /* D2D state compaction on retire (pegainfer issue #1001, Splits, "TP CUDA

@@ -18,7 +18,8 @@ from ._abi import GDN_BF16, GDN_F32, GdnError
 
 __all__ = ["Geometry", "LayerWeights", "StatePool", "GdnError", "gdn_slot_bytes",
            "gdn_prefill_scratch_bytes", "gdn_conv_update", "gdn_decode_batch",
-           "gdn_decode_step", "gdn_prefill_chunked", "gdn_state_compact", "library"]
+           "gdn_decode_step", "gdn_prefill_chunked", "gdn_state_compact", "gdn_linear",
+           "library"]
 
 
 def library():
@@ -221,3 +222,31 @@ def gdn_state_compact(geom: Geometry, pools: list[StatePool], src_host, dst_host
     _abi.check(lib.gdn_state_compact(
         ctypes.byref(g), arr, len(pools), s_hp, d_hp, _ptr(src, torch.int32, n, "src"),
         _ptr(dst, torch.int32, n, "dst"), n, _stream(stream)))
+
+
+def _rows(t: torch.Tensor, name: str) -> tuple[int, int, int]:
+    """(rows, cols, row stride) of a 2-D bf16 device tensor with unit column stride."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D bfloat16 tensor")
+    if t.stride(1) != 1 and t.size(1) > 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.size(0), t.size(1), t.stride(0) if t.size(0) > 1 else t.size(1)
+
+
+def gdn_linear(x: torch.Tensor, outs, stream=None) -> None:
+    """outs: 1..4 pairs (weight [N][K], out [M][N]); each out = x @ weight^T.
+    x and out may be row-strided views (unit column stride); weights are dense."""
+    lib = _abi.load()
+    M, K, ldx = _rows(x, "x")
+    arr = (_abi.gdn_linear_out * max(len(outs), 1))()
+    for i, (w, y) in enumerate(outs):
+        N, Kw, _ = _rows(w, f"weight {i}")
+        if not w.is_contiguous() or Kw != K:
+            raise ValueError(f"weight {i} must be a dense [N][{K}] tensor")
+        My, Ny, ldy = _rows(y, f"out {i}")
+        if My != M or Ny != N:
+            raise ValueError(f"out {i} must be [{M}][{N}]")
+        arr[i] = _abi.gdn_linear_out(w.data_ptr(), y.data_ptr(), N, ldy)
+    _abi.check(lib.gdn_linear(x.data_ptr(), M, K, ldx, arr, len(outs), _stream(stream)))

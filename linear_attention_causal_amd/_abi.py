@@ -52,6 +52,11 @@ class GdnError(RuntimeError):
         self.status = status
 
 
+class gdn_linear_out(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("N", ctypes.c_int32), ("ldy", ctypes.c_int32)]
+
+
 _lib = None
 
 _P = ctypes.c_void_p
@@ -74,6 +79,8 @@ PROTOTYPES = {
                                        _P]),
     "gdn_prefill_chunked": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _P, _P, _P, _I32, _P, _P,
                                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "gdn_linear": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.POINTER(gdn_linear_out), _I32,
+                                  _P]),
     "gdn_state_compact": (ctypes.c_int, [_GP, _PP, _I32, _P, _P, _P, _P, _I32, _P]),
 }
 

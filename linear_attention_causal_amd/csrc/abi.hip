@@ -279,4 +279,50 @@ int gdn_state_compact(const gdn_geometry* geom, const gdn_state_pool* pools, int
                     "gdn_state_compact launch");
 }
 
+int gdn_linear(const void* x, int32_t M, int32_t K, int32_t ldx, const gdn_linear_out* outs,
+               int32_t count, void* stream) {
+  if (M < 0 || K <= 0 || K % 8 != 0 || ldx < K || ldx % 8 != 0)
+    return fail(GDN_E_SHAPE, "need M >= 0, K > 0, K and ldx multiples of 8, ldx >= K");
+  if (count < 1 || count > gdn::kMaxLinearOuts)
+    return fail(GDN_E_SHAPE, "count must be in 1..%d", gdn::kMaxLinearOuts);
+  if (!outs) return fail(GDN_E_NULL, "outs is NULL");
+  if (M > 65535 * 16) return fail(GDN_E_SHAPE, "M too large");
+  if (M == 0) return ok();
+  if (!x) return fail(GDN_E_NULL, "x is NULL");
+  if (!aligned16(x)) return fail(GDN_E_ALIGN, "x must be 16-byte aligned");
+  // byte ranges [lo, hi) that outputs must not touch
+  struct Range { uintptr_t lo, hi; };
+  const auto range = [](const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+  };
+  const auto overlap = [](Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; };
+  std::vector<Range> reads{range(x, ((size_t)(M - 1) * ldx + K) * 2)}, writes;
+  gdn::LinearOut lo[gdn::kMaxLinearOuts];
+  long long tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    const gdn_linear_out& o = outs[i];
+    if (!o.weight || !o.out) return fail(GDN_E_NULL, "output %d has a NULL pointer", i);
+    if (o.N <= 0 || o.ldy < o.N) return fail(GDN_E_SHAPE, "output %d: need 0 < N <= ldy", i);
+    if (!aligned16(o.weight)) return fail(GDN_E_ALIGN, "weight %d must be 16-byte aligned", i);
+    if (reinterpret_cast<uintptr_t>(o.out) & 1u)
+      return fail(GDN_E_ALIGN, "output %d must be 2-byte aligned", i);
+    reads.push_back(range(o.weight, (size_t)o.N * K * 2));
+    writes.push_back(range(o.out, ((size_t)(M - 1) * o.ldy + o.N) * 2));
+    tiles += (o.N + 15) / 16;
+    lo[i] = gdn::LinearOut{static_cast<const __bf16*>(o.weight), static_cast<__bf16*>(o.out),
+                           o.N, o.ldy, 0};
+  }
+  if (tiles > 0x7fffffff) return fail(GDN_E_SHAPE, "too many output columns");
+  for (size_t i = 0; i < writes.size(); ++i) {
+    for (const Range& r : reads)
+      if (overlap(writes[i], r)) return fail(GDN_E_OVERLAP, "output %zu overlaps an input", i);
+    for (size_t j = i + 1; j < writes.size(); ++j)
+      if (overlap(writes[i], writes[j]))
+        return fail(GDN_E_OVERLAP, "outputs %zu and %zu overlap", i, j);
+  }
+  return hip_status(gdn::launch_linear(x, M, K, ldx, lo, count, static_cast<hipStream_t>(stream)),
+                    "gdn_linear launch");
+}
+
 }  // extern "C"

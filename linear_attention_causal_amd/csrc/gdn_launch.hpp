@@ -37,6 +37,19 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
                           const void* b, void* y, float* o_raw, void* scratch,
                           hipStream_t stream);
 
+// One weight of a projection launch: w [N][K] bf16, y [M][ldy] bf16.
+// tile0 is filled in by launch_linear.
+constexpr int kMaxLinearOuts = 4;
+struct LinearOut {
+  const __bf16* w;
+  __bf16* y;
+  int N, ldy, tile0;
+};
+// Rows per workgroup are 16 * linear_row_tiles(M).
+int linear_row_tiles(int M);
+hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* outs, int count,
+                         hipStream_t stream);
+
 hipError_t launch_compact(const gdn_geometry& g, const gdn_state_pool* pools, int L,
                           const int32_t* src, const int32_t* dst, int n,
                           hipStream_t stream);

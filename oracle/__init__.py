@@ -186,6 +186,45 @@ def pool_run(geom: Geometry, w: Weights, pool_S, pool_conv, cu_seqlens, slot_idx
     return y, o
 
 
+def linear(x, w):
+    """A projection: y[m][n] = sum_k x[m][k] w[n][k], with w stored [out][in]
+    like a Linear layer's weight.  These are the in_proj_qkv, in_proj_z,
+    in_proj_b, in_proj_a and out_proj products around the layer (cortex commit
+    95dc874, TpQwen3_5GatedDeltaNet bullet).  One f64 matrix product."""
+    return _f64(x) @ _f64(w).T
+
+
+@dataclass
+class Projections:
+    """Projection weights of one block, [out][in] each: qkv [C][H] (output in
+    [q | k | v] channel order), z [Hv*dv][H], b [Hv][H], a [Hv][H] and
+    out [H][Hv*dv] (cortex commit 95dc874, TpQwen3_5GatedDeltaNet bullet)."""
+    qkv: np.ndarray
+    z: np.ndarray
+    b: np.ndarray
+    a: np.ndarray
+    out: np.ndarray
+
+
+def decode_block(geom: Geometry, w: Weights, proj: Projections, pool_S, pool_conv, slot_idx,
+                 hidden, nthreads: int | None = None):
+    """One decode token per row through the whole block: the four input
+    projections of hidden [B][H], the layer on the slot pool (pool_run, which
+    updates the pools in place), then out_proj of the gated-norm output
+    (cortex commit 95dc874, TpQwen3_5GatedDeltaNet; the batched decode chain
+    of pegainfer PR #1003, PR body, batch_decode/prefill bullet).  No rounding
+    between the steps.  Returns (out [B][H], inputs, y [B][Hv][dv]) where
+    inputs holds the projected x, z, a, b."""
+    h = _f64(hidden)
+    B = h.shape[0]
+    Hv, dv = geom.num_v_heads, geom.head_v_dim
+    inp = dict(x=linear(h, proj.qkv), z=linear(h, proj.z).reshape(B, Hv, dv),
+               b=linear(h, proj.b), a=linear(h, proj.a))
+    y, _ = pool_run(geom, w, pool_S, pool_conv, np.arange(B + 1, dtype=np.int32), slot_idx,
+                    inp["x"], inp["z"], inp["a"], inp["b"], nthreads=nthreads)
+    return linear(y.reshape(B, Hv * dv), proj.out), inp, y
+
+
 def compact(geom: Geometry, pool_S, pool_conv, src, dst):
     """Copy slot src[i] to slot dst[i] (state and window), in place."""
     lib = _load()

@@ -34,7 +34,7 @@ def host_i32(vals):
 
 def test_exports_every_declared_function():
     names = _abi.header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(_abi.PROTOTYPES) == set(names)
@@ -161,3 +161,37 @@ def test_compact_checks():
     assert _compact([5, 8], [1, 2]) == _abi.GDN_E_SLOT          # out of range
     assert _compact([5, 6], [1, 5]) == _abi.GDN_E_OVERLAP
     assert _compact([5], [1], pools=[pool(8), pool(9)]) == _abi.GDN_E_SHAPE
+
+
+def _lin(M=16, K=64, ldx=64, outs=None, count=None, x=DEV):
+    if outs is None:
+        outs = [(V(0x200000), V(0x300000), 32, 32)]
+    arr = (_abi.gdn_linear_out * max(len(outs), 1))(
+        *[_abi.gdn_linear_out(w, y, n, ld) for (w, y, n, ld) in outs])
+    return lib.gdn_linear(x, M, K, ldx, arr, len(outs) if count is None else count, None)
+
+
+def test_linear_validation():
+    """Every check of gdn_linear returns before anything is enqueued."""
+    assert _lin(M=0, x=None) == _abi.GDN_OK                      # empty: no-op
+    assert _lin(M=-1) == _abi.GDN_E_SHAPE
+    assert _lin(K=60, ldx=64) == _abi.GDN_E_SHAPE                # K % 8
+    assert _lin(K=64, ldx=32) == _abi.GDN_E_SHAPE                # ldx < K
+    assert _lin(K=64, ldx=68) == _abi.GDN_E_SHAPE                # ldx % 8
+    assert _lin(count=0) == _abi.GDN_E_SHAPE
+    assert _lin(outs=[(V(0x200000), V(0x300000), 32, 32)] * 5) == _abi.GDN_E_SHAPE
+    assert _lin(x=None) == _abi.GDN_E_NULL
+    assert _lin(x=DEV_ODD) == _abi.GDN_E_ALIGN
+    assert _lin(outs=[(None, V(0x300000), 32, 32)]) == _abi.GDN_E_NULL
+    assert _lin(outs=[(V(0x200008), V(0x300000), 32, 32)]) == _abi.GDN_E_ALIGN
+    assert _lin(outs=[(V(0x200000), V(0x300001), 32, 32)]) == _abi.GDN_E_ALIGN
+    assert _lin(outs=[(V(0x200000), V(0x300000), 32, 16)]) == _abi.GDN_E_SHAPE   # ldy < N
+    assert _lin(outs=[(V(0x200000), V(0x300000), 0, 32)]) == _abi.GDN_E_SHAPE
+    # x spans [DEV, DEV + 2 (15 * 64 + 64)) = 2048 bytes: an output starting at
+    # its last element overlaps
+    assert _lin(outs=[(V(0x200000), V(0x100000 + 2046), 32, 32)]) == _abi.GDN_E_OVERLAP
+    # an output over a weight, and two outputs over each other
+    assert _lin(outs=[(V(0x200000), V(0x200000 + 64), 32, 32)]) == _abi.GDN_E_OVERLAP
+    assert _lin(outs=[(V(0x200000), V(0x300000), 32, 32),
+                      (V(0x400000), V(0x300000 + 1000), 32, 32)]) == _abi.GDN_E_OVERLAP
+    assert b"overlap" in lib.gdn_last_error()

@@ -392,3 +392,52 @@ def test_workload_generator_uses_bf16_grid():
     for arr in (w["conv_w"], inp["x"], inp["z"]):
         t = torch.from_numpy(arr)
         assert torch.equal(t.to(torch.bfloat16).to(torch.float32), t)
+
+
+# ------------------------------------------------------------------ projections
+
+def test_linear_matches_loops_on_non_square():
+    """y[m][n] = sum_k x[m][k] w[n][k] with w stored [out][in]: brute-force
+    loops on a 3 x 5 input and a 4 x 5 weight (a transposed operand or a
+    swapped product changes the shape or the values)."""
+    rng = np.random.default_rng(7)
+    x = rng.integers(-4, 5, (3, 5)).astype(np.float64)
+    w = rng.integers(-4, 5, (4, 5)).astype(np.float64)
+    ref = [[sum(x[m][k] * w[n][k] for k in range(5)) for n in range(4)] for m in range(3)]
+    y = oracle.linear(x, w)
+    assert y.shape == (3, 4)
+    np.testing.assert_array_equal(y, np.array(ref))
+
+
+def test_block_with_selection_projections_is_the_layer():
+    """With input projections that pick disjoint ranges of the hidden row and
+    an out_proj that copies y into the first Hv*dv outputs, the block equals
+    the layer run on those ranges as x, z, b, a (in that order), and the
+    remaining outputs are zero.  Pins which projection feeds which input."""
+    rng = np.random.default_rng(11)
+    C, Hv, dv = G.channels, G.num_v_heads, G.head_v_dim
+    vd = Hv * dv
+    H = C + vd + 2 * Hv
+    E = np.eye(H)
+    out = np.zeros((H, vd))
+    out[:vd] = np.eye(vd)
+    proj = oracle.Projections(qkv=E[:C], z=E[C:C + vd], b=E[C + vd:C + vd + Hv],
+                              a=E[C + vd + Hv:], out=out)
+    w, *_ = _rand_layer(rng, G, 1)
+    B, P = 5, 8
+    S = rng.normal(0, 0.3, (P, Hv, G.head_k_dim, dv))
+    W = rng.normal(size=(P, G.conv_kernel, C))
+    slots = rng.choice(P, B, replace=False).astype(np.int32)
+    h = rng.normal(size=(B, H))
+    S1, W1 = S.copy(), W.copy()
+    got, inp, y = oracle.decode_block(G, w, proj, S1, W1, slots, h)
+    S2, W2 = S.copy(), W.copy()
+    y_ref, _ = oracle.pool_run(G, w, S2, W2, np.arange(B + 1), slots, h[:, :C],
+                               h[:, C:C + vd].reshape(B, Hv, dv), h[:, C + vd + Hv:],
+                               h[:, C + vd:C + vd + Hv])
+    np.testing.assert_array_equal(y, y_ref)
+    np.testing.assert_array_equal(got[:, :vd], y_ref.reshape(B, vd))
+    assert not got[:, vd:].any()
+    np.testing.assert_array_equal(S1, S2)
+    np.testing.assert_array_equal(W1, W2)
+    np.testing.assert_array_equal(inp["a"], h[:, C + vd + Hv:])

@@ -17,6 +17,8 @@ Distributions (all workloads):
   conv weight ~ N(0, 0.25)
   norm weight = 1 + 0.1 N(0, 1)
   initial recurrent / conv states ~ N(0, 0.1) where a workload asks for them.
+  block workloads: hidden rows ~ N(0, 1); projection weights ~ N(0, 1/in)
+  in bf16, so the projected x, z, a, b are again about N(0, 1).
 """
 from __future__ import annotations
 
@@ -84,6 +86,22 @@ def state_pool(rng, s: Shape, P: int, std: float = 0.1, zero: bool = False):
     rec = (rng.standard_normal(rec_shape, dtype=np.float32) * np.float32(std))
     conv = _normal(rng, conv_shape, std, s.act)
     return rec, conv
+
+
+def bf16_normal(rng, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std) rounded to bfloat16 (float32 array)."""
+    return _normal(rng, shape, std, "bf16")
+
+
+def projection_weights(rng, s: Shape, hidden: int) -> dict:
+    """[out][in] bf16 weights: qkv [C][H], z [Hv*dv][H], b, a [Hv][H],
+    out [H][Hv*dv].  Draw order: qkv, z, b, a, out."""
+    vd = s.num_v_heads * s.head_v_dim
+    return dict(qkv=bf16_normal(rng, (s.channels, hidden), hidden ** -0.5),
+                z=bf16_normal(rng, (vd, hidden), hidden ** -0.5),
+                b=bf16_normal(rng, (s.num_v_heads, hidden), hidden ** -0.5),
+                a=bf16_normal(rng, (s.num_v_heads, hidden), hidden ** -0.5),
+                out=bf16_normal(rng, (hidden, vd), vd ** -0.5))
 
 
 # ------------------------------------------------------------- workloads
@@ -187,3 +205,28 @@ def retire_plan(rng, live_slots: np.ndarray, P: int):
     remap = dict(zip(movers, holes))
     new_slots = np.array([remap.get(int(s), int(s)) for s in kept], np.int32)
     return keep_mask, new_slots, np.array(movers, np.int32), np.array(holes, np.int32)
+
+
+# Hidden size of the block around the layer.  The pages give none; 2048 is the
+# published hidden size of Qwen3-Next, whose linear-attention layers have the
+# FULL_HEADS head counts (RANK_LOCAL is one rank of a two-way split of it).
+HIDDEN = 2048
+
+
+def decode_block(seed: int = 0, B: int = 16, P: int = 64, s: Shape = RANK_LOCAL,
+                 hidden: int = HIDDEN) -> Workload:
+    """One decode token per row through the whole block (input projections,
+    layer, out_proj): B rows drawn without replacement from P slots whose
+    states are N(0, 0.1); hidden rows [B][H].
+    Draw order: layer weights, projection weights, pools, slot_idx, hidden."""
+    if s.act != "bf16":
+        raise ValueError("the block runs on bf16 activations")
+    rng = np.random.default_rng(seed)
+    w = layer_weights(rng, s)
+    proj = projection_weights(rng, s, hidden)
+    rec, conv = state_pool(rng, s, P)
+    slot_idx = rng.choice(P, B, replace=False).astype(np.int32)
+    h = bf16_normal(rng, (B, hidden))
+    return Workload(f"block_b{B}_h{hidden}_hk{s.num_k_heads}_hv{s.num_v_heads}_d{s.head_k_dim}",
+                    s, seed, dict(weights=w, proj=proj, rec=rec, conv=conv, slot_idx=slot_idx,
+                                  hidden=h))
