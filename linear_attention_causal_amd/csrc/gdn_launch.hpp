@@ -45,8 +45,12 @@ struct LinearOut {
   __bf16* y;
   int N, ldy, tile0;
 };
-// Rows per workgroup are 16 * linear_row_tiles(M).
-int linear_row_tiles(int M);
+// Kernel and workgroup tile (rows x columns) launch_linear uses.
+struct LinearPlan {
+  enum Kind { kStream, kTile } kind;
+  int rows, cols;
+};
+LinearPlan linear_plan(int M, const LinearOut* outs, int count);
 hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* outs, int count,
                          hipStream_t stream);
 

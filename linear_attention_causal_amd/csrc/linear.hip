@@ -8,11 +8,18 @@
 // [N][K] like a Linear layer's weight.  One launch serves up to four
 // weights that read the same x (the four input projections of a token).
 //
-// At decode row counts this is a weight stream: every weight byte is used
-// by at most 16 * MT rows.  One workgroup of four waves per (16-column
-// tile, 16*MT-row block); each wave takes a quarter of K, requests its
-// weight and input fragments for a batch of k-steps before the first MFMA,
-// and the four partial tiles are added through LDS.
+// Two kernels, chosen by the row count M:
+//   stream (M <= 32, decode): a weight stream, each weight byte used by at
+//     most 32 rows.  A workgroup owns 16 or 32 output columns; its four
+//     waves split K and request every weight and input fragment of their K
+//     range before the first MFMA, and add their partial tiles through LDS.
+//   tile (M > 32): a dense product.  A workgroup owns a BM x BN output tile
+//     (the largest of 128 x 128, 128 x 64, 64 x 64 that still gives 128
+//     workgroups); x and w tiles of 32 k-columns are staged through three
+//     LDS buffers in MFMA fragment order, so each wave reads its operands
+//     with linear 16-byte LDS reads, and the input rows are fetched once
+//     per BN columns instead of once per 16.  Global loads run eight
+//     k-steps ahead in registers.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -22,81 +29,275 @@ namespace {
 
 typedef __bf16 lbf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kLinNT = 256;  // four waves
-
 struct LinParams {
   const __bf16* x;  // [M][ldx]
   int M, K, ldx, count;
   LinearOut out[kMaxLinearOuts];
 };
 
-template <int MT>
-__global__ __launch_bounds__(kLinNT) void linear_kernel(LinParams p) {
-  constexpr int KB = MT == 1 ? 16 : 8;  // k-steps requested at once per wave
-  __shared__ f32x4 s_part[4][MT][64];
-  // weight group of this column tile (blockIdx is uniform: scalar selects)
+// Weight group of column tile `tile` (uniform across the workgroup).
+__device__ __forceinline__ int group_of(const LinParams& p, int tile) {
   int g = 0;
 #pragma unroll
   for (int i = 1; i < kMaxLinearOuts; ++i)
-    if (i < p.count && (int)blockIdx.x >= p.out[i].tile0) g = i;
+    if (i < p.count && tile >= p.out[i].tile0) g = i;
+  return g;
+}
+
+__device__ __forceinline__ f32x4 mfma16(lbf16x8 a, lbf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Unconditional 16-byte load of 8 bf16.  Loads are never predicated: a
+// branch around a load makes the compiler drain every outstanding load at
+// the next use, so callers point a load that is not needed at a valid
+// address and zero its value where it is used.
+__device__ __forceinline__ lbf16x8 raw8(const __bf16* p) {
+  return *reinterpret_cast<const lbf16x8*>(p);
+}
+
+__device__ __forceinline__ lbf16x8 keep(lbf16x8 v, bool in) {
+  const lbf16x8 zero = {};
+  return in ? v : zero;
+}
+
+// Store the 16 x 16 tile s (MFMA D layout: D[i][j] at lane j + 16 (i / 4),
+// element i % 4) at rows m0.., columns n0.. with bounds guards.
+__device__ __forceinline__ void store_tile(const LinearOut& o, int M, int m0, int n0, int lane,
+                                           f32x4 s) {
+  const int n = n0 + (lane & 15);
+  if (n >= o.N) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = m0 + 4 * (lane >> 4) + e;
+    if (m < M) o.y[(size_t)m * o.ldy + n] = static_cast<__bf16>(s[e]);
+  }
+}
+
+template <int MT, int NT, int KW>
+__global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
+  constexpr int KB = MT + NT <= 3 ? 16 : 8;  // k-steps requested at once
+  __shared__ f32x4 s_part[KW][MT * NT][64];
+  const int g = group_of(p, blockIdx.x);
   const LinearOut o = p.out[g];
-  const int n0 = ((int)blockIdx.x - o.tile0) * 16, mb = blockIdx.y * 16 * MT;
+  const int n0 = ((int)blockIdx.x - o.tile0) * 16 * NT, mb = blockIdx.y * 16 * MT;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
   const int ksteps = (p.K + 31) / 32;
-  const int per = (ksteps + 3) / 4;
+  const int per = (ksteps + KW - 1) / KW;
   const int kb0 = wave * per, kb1 = min(ksteps, kb0 + per);
-  // A operand of tile t: rows mb + 16 t + li of x; B operand: row n0 + li of w.
-  // Lane li + 16 lk holds k = 32 ks + 8 lk .. +7.  Rows past M or N are
-  // clamped to the last one (read, never stored); k past K reads as zero.
+  // A operand of row tile t: rows mb + 16 t + li of x; B operand of column
+  // tile u: row n0 + 16 u + li of w.  Lane li + 16 lk holds k = 32 ks + 8 lk
+  // .. +7.  Rows past M or N are clamped to the last one (read, never
+  // stored); a k-chunk past K or a step past kb1 reads the row start and
+  // counts as zero.
   const __bf16* xr[MT];
+  const __bf16* wr[NT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xr[t] = p.x + (size_t)min(mb + 16 * t + li, p.M - 1) * p.ldx;
+#pragma unroll
+  for (int u = 0; u < NT; ++u) wr[u] = o.w + (size_t)min(n0 + 16 * u + li, o.N - 1) * p.K;
+  f32x4 acc[MT][NT];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
-    xr[t] = p.x + (size_t)min(mb + 16 * t + li, p.M - 1) * p.ldx + 8 * lk;
-  const __bf16* wr = o.w + (size_t)min(n0 + li, o.N - 1) * p.K + 8 * lk;
-  f32x4 acc[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const lbf16x8 zero = {};
+    for (int u = 0; u < NT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int kb = kb0; kb < kb1; kb += KB) {
-    lbf16x8 a[KB][MT], b[KB];
+    lbf16x8 a[KB][MT], b[KB][NT];
+    bool in[KB];
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      const int ks = min(kb + j, kb1 - 1);  // steps past kb1 are loaded, not used
-      const bool in = 32 * ks + 8 * lk < p.K;
-      b[j] = in ? *reinterpret_cast<const lbf16x8*>(wr + 32 * ks) : zero;
+      const int k = 32 * (kb + j) + 8 * lk;
+      in[j] = kb + j < kb1 && k < p.K;
+      const int off = in[j] ? k : 0;
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        a[j][t] = in ? *reinterpret_cast<const lbf16x8*>(xr[t] + 32 * ks) : zero;
+      for (int u = 0; u < NT; ++u) b[j][u] = raw8(wr[u] + off);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) a[j][t] = raw8(xr[t] + off);
     }
+    // keep the whole batch of loads in flight before the first MFMA (the
+    // scheduler would otherwise interleave them to save registers)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < KB; ++j)
-      if (kb + j < kb1) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][t], b[j], acc[t], 0, 0, 0);
-      }
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+          acc[t][u] = mfma16(keep(a[j][t], in[j]), b[j][u], acc[t][u]);
   }
 #pragma unroll
-  for (int t = 0; t < MT; ++t) s_part[wave][t][lane] = acc[t];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) s_part[wave][t * NT + u][lane] = acc[t][u];
   __syncthreads();
-  // wave t sums tile t; D[i][j] sits at lane j + 16 (i / 4), element i % 4
-  for (int t = wave; t < MT; t += 4) {
-    f32x4 s = s_part[0][t][lane];
+  for (int i = wave; i < MT * NT; i += KW) {
+    f32x4 s = s_part[0][i][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s += s_part[w][t][lane];
-    const int n = n0 + li;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = mb + 16 * t + 4 * lk + e;
-      if (m < p.M && n < o.N) o.y[(size_t)m * o.ldy + n] = static_cast<__bf16>(s[e]);
-    }
+    for (int w = 1; w < KW; ++w) s += s_part[w][i][lane];
+    store_tile(o, p.M, mb + 16 * (i / NT), n0 + 16 * (i % NT), lane, s);
   }
+}
+
+// BM x BN output tile, four waves as 2 x 2, each wave (BM/2) x (BN/2).
+// Global loads run D k-steps ahead of the MFMAs through a ring of D
+// register stages; each k-step is copied into one of three LDS buffers two
+// steps before its MFMAs, and its fragments are read from LDS one step
+// before, so LDS latency hides behind the previous step's MFMAs.
+template <int BM, int BN, int D>
+__global__ __launch_bounds__(256) void linear_tile_kernel(LinParams p) {
+  static_assert(D >= 3, "the ring holds the two k-steps ahead of the LDS copy");
+  constexpr int TM = BM / 32, TN = BN / 32;         // 16 x 16 tiles per wave
+  constexpr int XP = BM / 64, WP = BN / 64;         // 16-byte pieces per thread per k-step
+  // one k-step of each operand in fragment order: [16-row tile][lane] x 16 bytes
+  __shared__ lbf16x8 xs[3][BM / 16][64];
+  __shared__ lbf16x8 ws[3][BN / 16][64];
+  const int g = group_of(p, blockIdx.x);
+  const LinearOut o = p.out[g];
+  const int n0 = ((int)blockIdx.x - o.tile0) * BN, m0 = blockIdx.y * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ksteps = (p.K + 31) / 32;
+  // piece q = tid + 256 i: tile row r = q / 4, k-chunk c = q % 4 (the same c
+  // for every piece of a thread); its LDS slot is fragment r / 16, lane
+  // r % 16 + 16 c.  Rows past M or N are clamped (read, never stored); a
+  // k-chunk past K reads the row start, and the MFMAs zero it (a select on
+  // loaded data would make the compiler wait for the load where it places
+  // the select, which it hoists).
+  const int c = tid & 3;
+  const __bf16* xsrc[XP];
+  const __bf16* wsrc[WP];
+  int xslot[XP], wslot[WP];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int r = (tid + 256 * i) >> 2;
+    xsrc[i] = p.x + (size_t)min(m0 + r, p.M - 1) * p.ldx;
+    xslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < WP; ++i) {
+    const int r = (tid + 256 * i) >> 2;
+    wsrc[i] = o.w + (size_t)min(n0 + r, o.N - 1) * p.K;
+    wslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
+  }
+  lbf16x8 xr[D][XP], wr[D][WP];
+  const auto fetch = [&](int st, int ks) {
+    const int k = 32 * ks + 8 * c;
+    const int off = k < p.K ? k : 0;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) xr[st][i] = raw8(xsrc[i] + off);
+#pragma unroll
+    for (int i = 0; i < WP; ++i) wr[st][i] = raw8(wsrc[i] + off);
+  };
+  const auto put = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) (&xs[buf][0][0])[xslot[i]] = xr[st][i];
+#pragma unroll
+    for (int i = 0; i < WP; ++i) (&ws[buf][0][0])[wslot[i]] = wr[st][i];
+  };
+  // the k-step holding the end of K, when K is not a multiple of 32
+  const int tail = (p.K & 31) ? ksteps - 1 : -1;
+  const bool lane_in = 32 * tail + 8 * (lane >> 4) < p.K;
+  lbf16x8 fa[TM], fb[TN];
+  const auto frags = [&](int buf, lbf16x8* a, lbf16x8* b) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) a[t] = xs[buf][wm * TM + t][lane];
+#pragma unroll
+    for (int u = 0; u < TN; ++u) b[u] = ws[buf][wn * TN + u][lane];
+  };
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int u = 0; u < TN; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < D; ++d) fetch(d, d);
+  put(0, 0);
+  put(1, 1);
+  __syncthreads();
+  frags(0, fa, fb);
+  // Step ks: read k-step ks + 1's fragments (LDS buffer (ks + 1) % 3),
+  // MFMAs of k-step ks, copy k-step ks + 2 (ring stage (ks + 2) % D) into
+  // buffer (ks + 2) % 3, whose fragments were read two barriers ago, and
+  // fetch k-step ks + D into stage ks % D, copied to LDS two steps ago.
+  // Loads and copies always run (steps past K read row starts); in the
+  // guarded form the MFMAs of steps past K are skipped and the lanes of the
+  // K tail are zeroed.  The main loop takes only whole groups of D steps
+  // that lie inside K, so it has no branches for the scheduler to stop at.
+  const auto step = [&](int d, int ks, bool guarded) {
+    lbf16x8 na[TM], nb[TN];
+    frags((ks + 1) % 3, na, nb);
+    if (guarded && ks == tail) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) fa[t] = keep(fa[t], lane_in);
+#pragma unroll
+      for (int u = 0; u < TN; ++u) fb[u] = keep(fb[u], lane_in);
+    }
+    if (!guarded || ks < ksteps) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u) acc[t][u] = mfma16(fa[t], fb[u], acc[t][u]);
+    }
+    put((d + 2) % D, (ks + 2) % 3);
+    fetch(d, ks + D);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TM; ++t) fa[t] = na[t];
+#pragma unroll
+    for (int u = 0; u < TN; ++u) fb[u] = nb[u];
+  };
+  const int kfull = tail >= 0 ? tail : ksteps;  // steps without a K tail
+  int ks0 = 0;
+  for (; ks0 + D <= kfull; ks0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(d, ks0 + d, false);
+  }
+  for (; ks0 < ksteps; ks0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(d, ks0 + d, true);
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int u = 0; u < TN; ++u)
+      store_tile(o, p.M, m0 + 16 * (wm * TM + t), n0 + 16 * (wn * TN + u), lane, acc[t][u]);
+}
+
+template <typename Kern>
+hipError_t launch(Kern kern, LinParams p, const LinearOut* outs, int cols, int rows, int threads,
+                  hipStream_t stream) {
+  int tiles = 0;
+  for (int i = 0; i < kMaxLinearOuts; ++i) {
+    p.out[i] = i < p.count ? outs[i] : outs[0];
+    p.out[i].tile0 = tiles;
+    if (i < p.count) tiles += (outs[i].N + cols - 1) / cols;
+  }
+  kern<<<dim3(tiles, (p.M + rows - 1) / rows), threads, 0, stream>>>(p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-int linear_row_tiles(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+LinearPlan linear_plan(int M, const LinearOut* outs, int count) {
+  long long cols16 = 0, cols64 = 0, cols128 = 0;
+  for (int i = 0; i < count; ++i) {
+    cols16 += (outs[i].N + 15) / 16;
+    cols64 += (outs[i].N + 63) / 64;
+    cols128 += (outs[i].N + 127) / 128;
+  }
+  if (M <= 32) {
+    // two column tiles per workgroup once single tiles would fill the chip
+    // (halves the input-row reads per weight byte)
+    const int cols = cols16 >= 256 ? 32 : 16;
+    return {LinearPlan::kStream, M <= 16 ? 16 : 32, cols};
+  }
+  // the largest tile that still gives at least 128 workgroups
+  const long long rows128 = (M + 127) / 128;
+  if (cols128 * rows128 >= 128) return {LinearPlan::kTile, 128, 128};
+  if (cols64 * rows128 >= 128) return {LinearPlan::kTile, 128, 64};
+  return {LinearPlan::kTile, 64, 64};
+}
 
 hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* outs, int count,
                          hipStream_t stream) {
@@ -106,20 +307,19 @@ hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* 
   p.K = K;
   p.ldx = ldx;
   p.count = count;
-  int tiles = 0;
-  for (int i = 0; i < kMaxLinearOuts; ++i) {
-    p.out[i] = i < count ? outs[i] : outs[0];
-    p.out[i].tile0 = tiles;
-    if (i < count) tiles += (outs[i].N + 15) / 16;
+  const LinearPlan plan = linear_plan(M, outs, count);
+  if (plan.kind == LinearPlan::kStream) {
+    if (plan.rows == 16 && plan.cols == 16)
+      return launch(linear_stream_kernel<1, 1, 4>, p, outs, 16, 16, 256, stream);
+    if (plan.rows == 16) return launch(linear_stream_kernel<1, 2, 4>, p, outs, 32, 16, 256, stream);
+    if (plan.cols == 16) return launch(linear_stream_kernel<2, 1, 4>, p, outs, 16, 32, 256, stream);
+    return launch(linear_stream_kernel<2, 2, 4>, p, outs, 32, 32, 256, stream);
   }
-  const int mt = linear_row_tiles(M);
-  const dim3 grid(tiles, (M + 16 * mt - 1) / (16 * mt));
-  switch (mt) {
-    case 1: linear_kernel<1><<<grid, kLinNT, 0, stream>>>(p); break;
-    case 2: linear_kernel<2><<<grid, kLinNT, 0, stream>>>(p); break;
-    default: linear_kernel<4><<<grid, kLinNT, 0, stream>>>(p); break;
-  }
-  return hipGetLastError();
+  if (plan.rows == 128 && plan.cols == 128)
+    return launch(linear_tile_kernel<128, 128, 8>, p, outs, 128, 128, 256, stream);
+  if (plan.rows == 128)
+    return launch(linear_tile_kernel<128, 64, 8>, p, outs, 64, 128, 256, stream);
+  return launch(linear_tile_kernel<64, 64, 8>, p, outs, 64, 64, 256, stream);
 }
 
 }  // namespace gdn

@@ -53,6 +53,9 @@ def _run_linear(M, K, Ns, seed, x_pad=0, y_pad=0):
     (20, 200, [40, 8]),                   # two row tiles, K not a multiple of 32, ragged N
     (37, 96, [24, 17, 16, 3]),            # four row tiles, partial last block
     (100, 32, [100]),                     # K of one step: three waves have no work
+    (64, 200, [40, 8]),                   # tiled, K not a multiple of 32
+    (130, 72, [200, 5]),                  # tiled, partial row block and K tail
+    (512, 1024, [1024]),                  # tiled, large tile
 ])
 def test_linear(M, K, Ns):
     _run_linear(M, K, Ns, seed=M + K)
