@@ -40,6 +40,7 @@ HBM_PEAK = 8.0e12            # bytes/s
 BF16_PEAK = 2.5e15           # dense MFMA flop/s
 F32_MFMA_PEAK = 157.3e12     # dense f32 MFMA flop/s
 PREFILL_FLOP_PER_TOKEN_HEAD = 180_224   # chunk contractions at d = 128, L = 64
+GRAPH_PASSES = 4             # passes over the layer replicas per captured decode graph
 
 
 def log(msg):
@@ -150,19 +151,21 @@ def bench_decode(args):
     torch.cuda.synchronize()
     eager_dt = time.perf_counter() - t0
 
-    # graph: R steps (one per replica) captured once, replayed
+    # graph: G = GRAPH_PASSES * R steps (passes over the replicas) captured
+    # once, replayed; more steps per graph spread the replay's own launch cost
+    G = GRAPH_PASSES * R
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            for i in range(R):
+            for i in range(G):
                 step(i, side)
     stream.wait_stream(side)
-    for _ in range(max(1, args.warmup // R)):
+    for _ in range(max(1, args.warmup // G)):
         graph.replay()
     torch.cuda.synchronize()
-    reps = max(1, args.steps // R)
+    reps = max(1, args.steps // G)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     t0 = time.perf_counter()
@@ -172,8 +175,8 @@ def bench_decode(args):
         evs[k][1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    nsteps = reps * R
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / R
+    nsteps = reps * G
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / G
     per_launch = step_bytes(geom, B, 2)
     achieved = per_launch / (launch_ms * 1e-3)
     rec = recorded_traffic()
@@ -188,7 +191,8 @@ def bench_decode(args):
                   "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
                   "kernel": "gdn::decode_step_kernel<__bf16, 128, 2, 4>",
                   "bytes_per_launch": per_launch, "mean_launch_us": launch_ms * 1e3,
-                  "timing": "HIP events around graph replays of 16 back-to-back launches"},
+                  "timing": f"HIP events around graph replays of {G} back-to-back launches "
+                            f"({GRAPH_PASSES} passes over {R} replicas)"},
         step_hbm_frac=per_launch / (dt / nsteps) / HBM_PEAK)
 
 

@@ -322,6 +322,13 @@ __global__ __launch_bounds__(kStepThreadsPerDim * D * R) void decode_step_kernel
   }
   const float a_in = io::load(p.a, (size_t)row * p.Hv + h);
   const float b_in = io::load(p.b, (size_t)row * p.Hv + h);
+  // read here: below the window stores the compiler could not move these
+  // loads up (they might alias), and they would cost a second round trip
+  const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
+  // compiler-only fence: the small loads above are issued before the tile's,
+  // so the conv can start when they arrive (a wait counts loads in issue
+  // order); without it the conv loads get sunk below the tile's loads
+  asm volatile("" ::: "memory");
   float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
   f32x4 s[NQ][RPT];
 #pragma unroll
@@ -331,21 +338,28 @@ __global__ __launch_bounds__(kStepThreadsPerDim * D * R) void decode_step_kernel
       s[hf][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
           S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
 
-  // 2. conv + SiLU; shifted window written back (raw inputs: lossless)
+  // 2. conv + SiLU; shifted window written back (raw inputs: lossless).
+  // The sums are formed for every slot, outside the guard: used only inside
+  // it, the conv loads would be sunk below the tile's loads and, counted in
+  // order, wait for the whole tile.
+  float acc[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    acc[q] = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[q] = fmaf(wt[q][k], col[q][k], acc[q]);
+  }
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
     const int e = tid + q * NT;
     if (e < NCH) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < K; ++k) acc = fmaf(wt[q][k], col[q][k], acc);
-      s_x[e] = silu(acc);
+      s_x[e] = silu(acc[q]);
 #pragma unroll
       for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chs[q], col[q][k]);
     }
   }
   float g, beta;
-  gates(p.A_log[h], p.dt_bias[h], a_in, b_in, g, beta);
+  gates(A_log, dt_bias, a_in, b_in, g, beta);
   const float eg = expf(g);
   __syncthreads();
 
