@@ -448,7 +448,7 @@ __device__ __forceinline__ f32x4 mm16(const float* A, int lda, const float* B, i
 // wave of the workgroup; ends with the lower blocks of the result in sT (the strictly
 // upper blocks of sT are left as they are: the caller treats them as zero).
 template <int LDL>
-__device__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int tid) {
+__device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, float* sM, int tid) {
   const int lane = tid & 63, wave = wave_id();
   if (wave < 4 && lane < 16) {
     // column sweeps: once t_j is final, remove its term from every later row,
@@ -671,6 +671,22 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
   const int vgrp = tid % VG, vi_off = (tid / VG) * VTPT;
   ConvTile<Act, K, VTPT> vct;
   if (vact) vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
+  // k_hat^T fragments of this wave's W/U column blocks db = wave + kNW it
+  // (the A operand of W^T, from the q/k kernel), requested now, after every
+  // load the phases before W/U wait for, so their latency passes under the
+  // gates, A/P and the inverse
+  constexpr int DBW = (NDB + kNW - 1) / kNW;   // column blocks per wave
+  bf16x8 kth[DBW][2], ktl[DBW][2];
+#pragma unroll
+  for (int it = 0; it < DBW; ++it) {
+    const int db = min(wave + kNW * it, NDB - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const size_t at = frag_lane((gk * NDB + db) * 2 + ks, lane);
+      kth[it][ks] = ld8(p.s.kt[0] + at);
+      ktl[it][ks] = ld8(p.s.kt[1] + at);
+    }
+  }
   // gates: running sum gamma, beta, and the W row factor beta e^gamma
   if (wave == 0) {
     float gv = 0.f, bv = 0.f;
@@ -739,16 +755,13 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
       for (int t = 0; t < VTPT; ++t) sVt[(vgrp * VV + v) * LDL + vi_off + t] = vout[t][v];
   __syncthreads();
-  for (int db = wave; db < NDB; db += kNW) {
-    const int d = 16 * db + li;
-    // k_hat^T rows d (A operand of W^T), from the q/k kernel
-    bf16x8 kh[2], kl[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const size_t at = frag_lane((gk * NDB + db) * 2 + ks, lane);
-      kh[ks] = ld8(p.s.kt[0] + at);
-      kl[ks] = ld8(p.s.kt[1] + at);
-    }
+  for (int it = 0; it < DBW; ++it) {
+    const int db = wave + kNW * it;
+    if (db >= NDB) break;   // uniform: fewer column blocks than waves
+    const int d = 16 * db + li;
+    const bf16x8* kh = kth[it];
+    const bf16x8* kl = ktl[it];
     // v^T rows d, split (B operand of U)
     bf16x8 vh[2], vl[2];
 #pragma unroll
@@ -848,20 +861,36 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   const size_t cbase = si.len > 0 ? chunk_base_of(p, n) : 0;
   const int nchunks = (si.len + kL - 1) / kL;
 
+  // S_0: every load of a recurrence wave is issued before any is used (row
+  // blocks past the state are clamped and dropped), and a slot without an
+  // initial state is masked to zero bit by bit.  A branch or a select there
+  // would make the compiler test has_init first and wait for each block's
+  // loads before issuing the next.
   f32x4 S[RBW][NCB];
 #pragma unroll
-  for (int q = 0; q < RBW; ++q) {
-    const int rb = w4 + 4 * q;
+  for (int q = 0; q < RBW; ++q)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      S[q][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (rec && rb < NRB)
+    for (int cb = 0; cb < NCB; ++cb) S[q][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (rec) {
+    float v[RBW][NCB][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li];
-          S[q][cb][e] = si.init ? v : 0.f;
-        }
+    for (int q = 0; q < RBW; ++q) {
+      const int rb = min(w4 + 4 * q, NRB - 1);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[q][cb][e] = Sg[(size_t)(16 * rb + 4 * lk + e) * D + col0 + 16 * cb + li];
     }
+    const unsigned keep_bits = si.init ? ~0u : 0u;
+#pragma unroll
+    for (int q = 0; q < RBW; ++q)
+      if (w4 + 4 * q < NRB)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S[q][cb][e] = __uint_as_float(__float_as_uint(v[q][cb][e]) & keep_bits);
   }
 
   // Loads are unconditional within a wave's role (chunk index clamped), so
