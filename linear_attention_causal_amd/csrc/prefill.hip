@@ -805,6 +805,9 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
 constexpr int kSW = 8;             // waves of the state kernel
 constexpr int kSNT = 64 * kSW;
 
+// Compile-time wave role of the state kernel's chunk loop.
+template <bool B> struct WaveRole { static constexpr bool value = B; };
+
 // Operands of one chunk held in registers by one wave of the state kernel;
 // the next chunk's are fetched into the same registers right after their
 // last use.  The same registers serve both wave roles:
@@ -893,48 +896,6 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
             S[q][cb][e] = __uint_as_float(__float_as_uint(v[q][cb][e]) & keep_bits);
   }
 
-  // Loads are unconditional within a wave's role (chunk index clamped), so
-  // the prefetch of chunk c+1 never introduces a branch and its wait.
-  auto load_fa = [&](ChunkOps<NKS, RBW, NCB>& o, int c) {
-    const size_t mat = rec ? (cbase + c) * p.Hv + h : (cbase + c) * p.Hk + m;
-    const __bf16* hi = rec ? p.s.w[0] : p.s.qh[0];
-    const __bf16* lo = rec ? p.s.w[1] : p.s.qh[1];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const size_t at = frag_lane(mat * (4 * NKS) + w4 * NKS + ks, lane);
-      o.fa[ks][0] = ld8(hi + at);
-      o.fa[ks][1] = ld8(lo + at);
-    }
-  };
-  auto load_fb = [&](ChunkOps<NKS, RBW, NCB>& o, int c) {
-    const __bf16* hi = rec ? p.s.kt[0] : p.s.pm[0];
-    const __bf16* lo = rec ? p.s.kt[1] : p.s.pm[1];
-#pragma unroll
-    for (int q = 0; q < RBW; ++q) {
-      if (!rec && q > 0) break;   // uniform: output waves need one P row block
-      const int rb = min(w4 + 4 * q, NRB - 1);
-      const size_t blk0 = rec ? (((cbase + c) * p.Hk + m) * NRB + rb) * 2
-                              : (((cbase + c) * p.Hv + h) * 4 + w4) * 2;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const size_t at = frag_lane(blk0 + ks, lane);
-        o.fb[q][ks][0] = ld8(hi + at);
-        o.fb[q][ks][1] = ld8(lo + at);
-      }
-    }
-  };
-  auto load_misc = [&](ChunkOps<NKS, RBW, NCB>& o, int c) {
-    const int nc = min(kL, si.len - c * kL);
-    const size_t gh = (cbase + c) * p.Hv + h;
-    if (rec)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        o.u[cb] = *reinterpret_cast<const f32x4*>(
-            p.s.ut + (((gh * NRB + col0 / 16 + cb) * 4 + w4) * 64 + lane) * 4);
-    o.gam = *reinterpret_cast<const f32x4*>(p.s.gam + gh * kL + i0);
-    o.glast = p.s.gam[gh * kL + nc - 1];
-  };
-
   // S_0 into LDS as hi/lo bf16, columns major
   if (rec)
 #pragma unroll
@@ -951,102 +912,158 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
             sS[1][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = lo;
           }
     }
-  ChunkOps<NKS, RBW, NCB> ops;
-  if (nchunks > 0) {  // same issue order as in the loop (see its waits)
-    load_misc(ops, 0);
-    load_fa(ops, 0);
-    load_fb(ops, 0);
-  }
-  __syncthreads();
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = c * kL, nc = min(kL, si.len - t0);
-    const long long tok0 = si.begin + t0;
-    const int cn = min(c + 1, nchunks - 1);  // chunk whose operands are prefetched
-    // U and gamma are needed first: take them and refetch for the next chunk
-    // at once, so their loads are the oldest outstanding ones a chunk later
-    f32x4 u[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) u[cb] = ops.u[cb];
-    const f32x4 gam = ops.gam;
-    const float glast = ops.glast;
-    load_misc(ops, cn);
-    // phase 1: V' = U - W S_c (recurrence waves) / Y = Q S_c (output waves)
-    f32x4 O[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      Acc3 acc = acc3(rec ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+  // The chunk loop, instantiated once per wave role (REC: the recurrence
+  // waves).  With the role a compile-time constant the loop holds no role
+  // branch, so the registers a role carries from chunk to chunk are never
+  // merged with the other role's; such a merge copies just-loaded registers
+  // and so waits for their loads at once.  Both instantiations pass the same
+  // barriers in the same order.  Loads are unconditional within a role
+  // (chunk index clamped), so the prefetch of chunk c+1 never introduces a
+  // branch and its wait.
+  const auto chunk_loop = [&](auto role) {
+    constexpr bool REC = decltype(role)::value;
+    ChunkOps<NKS, RBW, NCB> ops;
+    auto load_fa = [&](int c) {
+      const size_t mat = REC ? (cbase + c) * p.Hv + h : (cbase + c) * p.Hk + m;
+      const __bf16* hi = REC ? p.s.w[0] : p.s.qh[0];
+      const __bf16* lo = REC ? p.s.w[1] : p.s.qh[1];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
-        mfma3(acc, ops.fa[ks][0], ops.fa[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]));
+        const size_t at = frag_lane(mat * (4 * NKS) + w4 * NKS + ks, lane);
+        ops.fa[ks][0] = ld8(hi + at);
+        ops.fa[ks][1] = ld8(lo + at);
       }
-      const f32x4 r1 = fold(acc);
-      if (rec) {
+    };
+    auto load_fb = [&](int c) {
+      const __bf16* hi = REC ? p.s.kt[0] : p.s.pm[0];
+      const __bf16* lo = REC ? p.s.kt[1] : p.s.pm[1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * cb + li, i = i0 + e;
-          __bf16 hi, lo;
-          split_bf16(r1[e], hi, lo);
-          sV[0][j * LR + i] = hi;
-          sV[1][j * LR + i] = lo;
-          split_bf16(__expf(glast - gam[e]) * r1[e], hi, lo);
-          sD[0][j * LR + i] = hi;
-          sD[1][j * LR + i] = lo;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[cb][e] = __expf(gam[e]) * r1[e];
-      }
-    }
-    load_fa(ops, cn);
-    __syncthreads();  // V' is in LDS; every read of S_c is done
-    if (rec) {
-      // phase 2: S <- e^{gamma_L} S + K^T (e^{gamma_L - gamma} V')
-      const float egl = __expf(glast);
-#pragma unroll
-      for (int q = 0; q < RBW; ++q) {
-        const int rb = w4 + 4 * q;
-        if (rb < NRB)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            Acc3 as = acc3(S[q][cb] * egl);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-              mfma3(as, ops.fb[q][ks][0], ops.fb[q][ks][1], ld8(&sD[0][bo]), ld8(&sD[1][bo]));
-            }
-            S[q][cb] = fold(as);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              __bf16 hi, lo;
-              split_bf16(S[q][cb][e], hi, lo);
-              sS[0][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = hi;
-              sS[1][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = lo;
-            }
-          }
-      }
-    } else {
-      // O += P V', stored as the pre-norm output
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        Acc3 ao = acc3(O[cb]);
+      for (int q = 0; q < (REC ? RBW : 1); ++q) {   // output waves need one P row block
+        const int rb = min(w4 + 4 * q, NRB - 1);
+        const size_t blk0 = REC ? (((cbase + c) * p.Hk + m) * NRB + rb) * 2
+                                : (((cbase + c) * p.Hv + h) * 4 + w4) * 2;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-          mfma3(ao, ops.fb[0][ks][0], ops.fb[0][ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]));
-        }
-        const f32x4 o = fold(ao);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          if (i < nc) p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li] = o[e];
+          const size_t at = frag_lane(blk0 + ks, lane);
+          ops.fb[q][ks][0] = ld8(hi + at);
+          ops.fb[q][ks][1] = ld8(lo + at);
         }
       }
+    };
+    auto load_misc = [&](int c) {
+      const int nc = min(kL, si.len - c * kL);
+      const size_t gh = (cbase + c) * p.Hv + h;
+      if constexpr (REC)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          ops.u[cb] = *reinterpret_cast<const f32x4*>(
+              p.s.ut + (((gh * NRB + col0 / 16 + cb) * 4 + w4) * 64 + lane) * 4);
+      ops.gam = *reinterpret_cast<const f32x4*>(p.s.gam + gh * kL + i0);
+      ops.glast = p.s.gam[gh * kL + nc - 1];
+    };
+
+    if (nchunks > 0) {  // same issue order as in the loop (see its waits)
+      load_misc(0);
+      load_fa(0);
+      load_fb(0);
     }
-    load_fb(ops, cn);
-    __syncthreads();  // S_{c+1} is in LDS; every read of V' is done
-  }
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+      const int t0 = c * kL, nc = min(kL, si.len - t0);
+      const long long tok0 = si.begin + t0;
+      const int cn = min(c + 1, nchunks - 1);  // chunk whose operands are prefetched
+      // U and gamma are needed first: take them and refetch for the next
+      // chunk at once, so their loads are the oldest outstanding ones a
+      // chunk later
+      f32x4 u[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) u[cb] = ops.u[cb];
+      const f32x4 gam = ops.gam;
+      const float glast = ops.glast;
+      load_misc(cn);
+      // phase 1: V' = U - W S_c (recurrence waves) / Y = Q S_c (output waves)
+      f32x4 O[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        Acc3 acc = acc3(REC ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
+          mfma3(acc, ops.fa[ks][0], ops.fa[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]));
+        }
+        const f32x4 r1 = fold(acc);
+        if constexpr (REC) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * cb + li, i = i0 + e;
+            __bf16 hi, lo;
+            split_bf16(r1[e], hi, lo);
+            sV[0][j * LR + i] = hi;
+            sV[1][j * LR + i] = lo;
+            split_bf16(__expf(glast - gam[e]) * r1[e], hi, lo);
+            sD[0][j * LR + i] = hi;
+            sD[1][j * LR + i] = lo;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[cb][e] = __expf(gam[e]) * r1[e];
+        }
+      }
+      load_fa(cn);
+      __syncthreads();  // V' is in LDS; every read of S_c is done
+      if constexpr (REC) {
+        // phase 2: S <- e^{gamma_L} S + K^T (e^{gamma_L - gamma} V')
+        const float egl = __expf(glast);
+#pragma unroll
+        for (int q = 0; q < RBW; ++q) {
+          const int rb = w4 + 4 * q;
+          if (rb < NRB)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              Acc3 as = acc3(S[q][cb] * egl);
+#pragma unroll
+              for (int ks = 0; ks < 2; ++ks) {
+                const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+                mfma3(as, ops.fb[q][ks][0], ops.fb[q][ks][1], ld8(&sD[0][bo]), ld8(&sD[1][bo]));
+              }
+              S[q][cb] = fold(as);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                __bf16 hi, lo;
+                split_bf16(S[q][cb][e], hi, lo);
+                sS[0][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = hi;
+                sS[1][(16 * cb + li) * LS + 16 * rb + 4 * lk + e] = lo;
+              }
+            }
+        }
+      } else {
+        // O += P V', stored as the pre-norm output
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          Acc3 ao = acc3(O[cb]);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+            mfma3(ao, ops.fb[0][ks][0], ops.fb[0][ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]));
+          }
+          const f32x4 o = fold(ao);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            if (i < nc) p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li] = o[e];
+          }
+        }
+      }
+      load_fb(cn);
+      __syncthreads();  // S_{c+1} is in LDS; every read of V' is done
+    }
+  };
+  if (rec)
+    chunk_loop(WaveRole<true>{});
+  else
+    chunk_loop(WaveRole<false>{});
 
   if (rec)
 #pragma unroll
