@@ -222,10 +222,14 @@ struct ChanReader {
   }
 
   // The 16 bytes starting at this channel (16 / element-size consecutive
-  // channels) at `pos`, same rules; the caller zeroes them when !use.
-  __device__ __forceinline__ u32x4 fetch16(int pos, bool valid, bool& use) const {
+  // channels) at `pos`.  Here `use` leaves out whether the slot holds an
+  // initial window (the address must not wait for that flag): `win` marks a
+  // window position, and the caller zeroes the bytes when !use, or when win
+  // and the sequence starts fresh.
+  __device__ __forceinline__ u32x4 fetch16(int pos, bool valid, bool& use, bool& win) const {
     const bool in_x = pos >= 0;
-    use = valid & (in_x ? pos < len : (init & (pos >= -K)));
+    use = valid & (in_x ? pos < len : pos >= -K);
+    win = !in_x;
     const int pc = use ? pos : (in_x ? 0 : -1);
     const char* a = (in_x ? xb : wb) + (long long)pc * stride;
     return *reinterpret_cast<const u32x4*>(a);
@@ -258,18 +262,23 @@ struct ConvTile {
   static constexpr int V = 16 / sizeof(Act);
   u32x4 raw[TPT + K - 1];
   u32x4 wraw[K];
-  uint32_t use;   // bit j: input run j is part of the input
+  uint32_t use;   // bit j: input run j is part of the input (window runs: if init)
+  uint32_t win;   // bit j: input run j lies in the slot's conv window
+  bool init;      // the window holds an initial state (applied in finish)
 
   __device__ __forceinline__ void fetch(const PrefillParams& p, const SeqInfo& si, int t0,
                                         int nc, int i_off, int ch) {
     const ChanReader<Act, K> rd(p, si, ch);
     use = 0;
+    win = 0;
+    init = si.init;
 #pragma unroll
     for (int j = 0; j < TPT + K - 1; ++j) {
       const int r = i_off - (K - 1) + j;   // relative to the chunk start
-      bool u;
-      raw[j] = rd.fetch16(t0 + r, r < nc, u);
+      bool u, w;
+      raw[j] = rd.fetch16(t0 + r, r < nc, u, w);
       use |= (uint32_t)u << j;
+      win |= (uint32_t)w << j;
     }
     // weights of the V channels: V * K consecutive elements = K runs of 16 bytes
     const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.conv_w) +
@@ -282,12 +291,13 @@ struct ConvTile {
     float wt[V * K];   // wt[v * K + k]
 #pragma unroll
     for (int k = 0; k < K; ++k) unpack16<Act>(wraw[k], wt + k * V);
+    const uint32_t eff = init ? use : use & ~win;
     float xs[TPT + K - 1][V];
 #pragma unroll
     for (int j = 0; j < TPT + K - 1; ++j) {
       unpack16<Act>(raw[j], xs[j]);
 #pragma unroll
-      for (int v = 0; v < V; ++v) xs[j][v] = (use >> j) & 1u ? xs[j][v] : 0.f;
+      for (int v = 0; v < V; ++v) xs[j][v] = (eff >> j) & 1u ? xs[j][v] : 0.f;
     }
 #pragma unroll
     for (int t = 0; t < TPT; ++t)
