@@ -119,20 +119,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   }
   const int m = h / p.r;  // K-head read by V-head h (repeat_interleave)
 
-  // q, k (K-head m) and v (V-head h): issued before the state tile
+  // q, k (K-head m) and v (V-head h) and the gate inputs: issued before the
+  // state tile, unconditionally (indices past 3D are clamped and their
+  // values dropped; a load under a branch would be waited for at once)
   const float* xr = p.qkv + (size_t)row * p.C;
   float tmp[QKV_PER];
 #pragma unroll
   for (int e = 0; e < QKV_PER; ++e) {
-    const int j = tid + e * NT;
-    if (j < 3 * D) {
-      const int part = j / D, jj = j - part * D;
-      const size_t off = part == 0 ? (size_t)m * D + jj
-                       : part == 1 ? (size_t)(p.Hk + m) * D + jj
-                                   : (size_t)2 * p.Hk * D + (size_t)h * D + jj;
-      tmp[e] = xr[off];
-    }
+    const int j = min(tid + e * NT, 3 * D - 1);
+    const int part = j / D, jj = j - part * D;
+    const size_t off = part == 0 ? (size_t)m * D + jj
+                     : part == 1 ? (size_t)(p.Hk + m) * D + jj
+                                 : (size_t)2 * p.Hk * D + (size_t)h * D + jj;
+    tmp[e] = xr[off];
   }
+  const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
+  const float a_in = io::load(p.a, (size_t)row * p.Hv + h);
+  const float b_in = io::load(p.b, (size_t)row * p.Hv + h);
   float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
   f32x4 s[RPT];
 #pragma unroll
@@ -141,8 +144,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         reinterpret_cast<const f32x4*>(S + (size_t)(rg + RG * i) * D + 4 * cg));
 
   float g, beta;
-  gates(p.A_log[h], p.dt_bias[h], io::load(p.a, (size_t)row * p.Hv + h),
-        io::load(p.b, (size_t)row * p.Hv + h), g, beta);
+  gates(A_log, dt_bias, a_in, b_in, g, beta);
   const float eg = expf(g);
 
 #pragma unroll
