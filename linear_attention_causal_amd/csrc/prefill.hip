@@ -157,14 +157,53 @@ struct SeqInfo {
   bool init;
 };
 
+// Device copy of an index array read in the branch beside an inline one: the
+// volatile read keeps the compiler from merging the two branches into one
+// load through a select of the two addresses (a generic pointer whose load
+// waits a vector-memory round trip; the inline read alone is a scalar load).
+__device__ __forceinline__ long long read_dev(const int32_t* a, int i) {
+  return *reinterpret_cast<const volatile int32_t*>(a + i);
+}
+
 // First scratch chunk of sequence n.
 __device__ __forceinline__ size_t chunk_base_of(const PrefillParams& p, int n) {
-  return p.inl ? (size_t)p.inl_cb[n] : (size_t)p.s.chunk_base[n];
+  if (p.inl) return (size_t)p.inl_cb[n];
+  return (size_t)read_dev(p.s.chunk_base, n);
+}
+
+// (sequence n, chunk c) of this workgroup for the per-chunk kernels.  A
+// launch that carries the chunk prefix enumerates only real chunks along x
+// (packed varlen batches would otherwise launch max_chunks per sequence,
+// mostly empty workgroups that still read their sequence's bounds); n is
+// the last sequence whose first chunk is at or before x.  Otherwise x is
+// the chunk and y the sequence.
+__device__ __forceinline__ void chunk_of(const PrefillParams& p, int& n, int& c) {
+  if (p.inl) {
+    const int g = blockIdx.x;
+    int lo = 0, hi = p.N;   // inl_cb[lo] <= g < inl_cb[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.inl_cb[mid] <= g) lo = mid;
+      else hi = mid;
+    }
+    n = lo;
+    c = g - p.inl_cb[lo];
+  } else {
+    c = blockIdx.x;
+    n = blockIdx.y;
+  }
 }
 
 __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int n) {
   SeqInfo s;
-  long long b = p.inl ? p.inl_cu[n] : p.cu[n], e = p.inl ? p.inl_cu[n + 1] : p.cu[n + 1];
+  long long b, e;
+  if (p.inl) {
+    b = p.inl_cu[n];
+    e = p.inl_cu[n + 1];
+  } else {
+    b = read_dev(p.cu, n);
+    e = read_dev(p.cu, n + 1);
+  }
   if (b < 0 || e > p.T || e < b) { b = 0; e = 0; }  // inconsistent copy: treat as empty
   if (!p.inl && e > b &&
       (size_t)p.s.chunk_base[n] + (size_t)((e - b + kL - 1) / kL) > p.G) {
@@ -510,7 +549,9 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k rows (unnormalized)
   __shared__ float sRq[kL], sRk[kL];
 
-  const int c = blockIdx.x, n = blockIdx.y, m = blockIdx.z;
+  int n, c;
+  chunk_of(p, n, c);
+  const int m = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
   if (si.slot < 0 || t0 >= si.len) return;
@@ -633,7 +674,9 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
   float* sT = sAT + kL * LDL;
   float* sVt = sAT;
 
-  const int c = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
+  int n, c;
+  chunk_of(p, n, c);
+  const int h = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
   if (si.slot < 0 || t0 >= si.len) return;
@@ -1122,7 +1165,9 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   constexpr int VPL = D / 32;      // values per lane
   constexpr int ROWS = kNT / 32;   // rows per pass
   constexpr int NP = kL / ROWS;    // passes
-  const int c = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
+  int n, c;
+  chunk_of(p, n, c);
+  const int h = blockIdx.z;
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
   if (t0 >= si.len) return;
@@ -1216,9 +1261,11 @@ template <typename Act, int D, int K>
 static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_t st) {
   // (with no tokens there are no chunks and the scratch may be absent)
   if (!p.inl && p.T > 0) prefill_plan_kernel<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.s.chunk_base);
+  // per-chunk grid: the real chunks when the prefix travels with the launch
+  const dim3 chunks = p.inl ? dim3(p.inl_cb[p.N], 1) : dim3(max_chunks, p.N);
   if (max_chunks > 0) {
-    prefill_qk_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hk), kNT, 0, st>>>(p);
-    prefill_wy_kernel<Act, D, K><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
+    prefill_qk_kernel<Act, D, K><<<dim3(chunks.x, chunks.y, p.Hk), kNT, 0, st>>>(p);
+    prefill_wy_kernel<Act, D, K><<<dim3(chunks.x, chunks.y, p.Hv), kNT, 0, st>>>(p);
   }
   switch (state_col_blocks(p.N, p.Hv, D)) {
     case 1: launch_state<Act, D, K, 1>(p, st); break;
@@ -1227,7 +1274,7 @@ static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_
     default: return hipErrorInvalidValue;
   }
   if (max_chunks > 0)
-    prefill_norm_kernel<Act, D><<<dim3(max_chunks, p.N, p.Hv), kNT, 0, st>>>(p);
+    prefill_norm_kernel<Act, D><<<dim3(chunks.x, chunks.y, p.Hv), kNT, 0, st>>>(p);
   return hipGetLastError();
 }
 
