@@ -21,9 +21,9 @@
 //   0. plan   one workgroup: chunk_base[n] = number of chunks before sequence n
 //             (only for batches of more than kInlineSeqs sequences; smaller
 //             ones carry the prefix, taken from the host copy, in the launch).
-//   1. q/k    (chunk, sequence, K-head), all chunks in parallel: conv + SiLU
-//             of q/k, l2 norms, q_hat and k_hat^T fragments, K K^T and Q K^T.
-//   1'. WY    (chunk, sequence, V-head), all chunks in parallel: the gates and
+//   1. q/k    (chunk, K-head), all chunks in parallel: conv + SiLU of q/k, l2
+//             norms, q_hat and k_hat^T fragments, K K^T and Q K^T.
+//   1'. WY    (chunk, V-head), all chunks in parallel: the gates and
 //             their running sum, A, P, Tm (blocked 16 x 16 triangular
 //             inverse), conv + SiLU of v, W and U.  Operands are written as
 //             bf16 (hi, lo) pairs (U as f32) in the fragment layout of the
@@ -35,7 +35,10 @@
 //             the other half, on 3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo
 //             + lo*hi with f32 accumulation, about 2^-16 relative), O
 //             (pre-norm) to f32.
-//   3. norm   (chunk, sequence, V-head): gated RMSNorm with SiLU(z) -> y.
+//   3. norm   (chunk, V-head): gated RMSNorm with SiLU(z) -> y.
+// The per-chunk launches (1, 1', 3) cover the real chunks of the batch when
+// the prefix travels with the launch, else every (chunk slot, sequence) pair
+// up to the longest sequence (see chunk_of).
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -50,7 +53,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Chunk-indexed scratch: chunk g = chunk_base[n] + c holds 64 rows (rows past
-// the end of a sequence are written as zeros by the prep kernel).  Everything
+// the end of a sequence are written as zeros by the q/k and WY kernels).  Everything
 // the sequential state kernel reads is stored fragment-major (see frag_at):
 // one wave's MFMA operand tile is one contiguous 1 KB block.
 struct PrefillScratch {
