@@ -1158,16 +1158,19 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------------ 3. norm
 
-// 256 threads = 8 token rows x 32 lanes; a lane owns D/32 consecutive values
-// of each of the chunk's rows r, r + 8, ...  Every load of the chunk (the
-// pre-norm output and z, rows clamped to the chunk so no load is
-// conditional) is requested before any arithmetic.
+// 256 threads = ROWS token rows x LPR lanes; a lane owns 8 consecutive values
+// of each of the chunk's rows r, r + ROWS, ... (16-byte runs of z and y in
+// bf16, 32 bytes of the f32 pre-norm output).  Every load of the chunk (rows
+// clamped to the chunk so no load is conditional) is requested before any
+// arithmetic.
 template <typename Act, int D>
 __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   using io = act_io<Act>;
-  constexpr int VPL = D / 32;      // values per lane
-  constexpr int ROWS = kNT / 32;   // rows per pass
+  constexpr int VPL = 8;           // values per lane
+  constexpr int LPR = D / VPL;     // lanes per row
+  constexpr int ROWS = kNT / LPR;  // rows per pass
   constexpr int NP = kL / ROWS;    // passes
+  static_assert(64 % LPR == 0 && kL % ROWS == 0, "norm split");
   int n, c;
   chunk_of(p, n, c);
   const int h = blockIdx.z;
@@ -1176,7 +1179,7 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   if (t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
   const long long tok0 = si.begin + t0;
-  const int tid = threadIdx.x, sub = tid & 31, rr = tid >> 5;
+  const int tid = threadIdx.x, sub = tid % LPR, rr = tid / LPR;
   const int d0 = sub * VPL;
   if (si.slot < 0) {  // padding sequence: zero outputs
     for (int pass = 0; pass < NP; ++pass) {
@@ -1191,50 +1194,40 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
     }
     return;
   }
-  float ov[NP][VPL], zv[NP][VPL];
+  f32x4 ov[NP][2], zv[NP][2];
 #pragma unroll
   for (int pass = 0; pass < NP; ++pass) {
     const int i = min(pass * ROWS + rr, nc - 1);
     const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0;
-    if constexpr (VPL == 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.obuf + o);
-      const f32x4 z = io::load4(p.z, o);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        ov[pass][k] = v[k];
-        zv[pass][k] = z[k];
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        ov[pass][k] = p.obuf[o + k];
-        zv[pass][k] = io::load(p.z, o + k);
-      }
+    for (int hf = 0; hf < 2; ++hf) {
+      ov[pass][hf] = *reinterpret_cast<const f32x4*>(p.obuf + o + 4 * hf);
+      zv[pass][hf] = io::load4(p.z, o + 4 * hf);
     }
   }
-  float nw[VPL];
+  f32x4 nw[2];
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) nw[k] = p.norm_w[d0 + k];
+  for (int hf = 0; hf < 2; ++hf) nw[hf] = *reinterpret_cast<const f32x4*>(p.norm_w + d0 + 4 * hf);
 #pragma unroll
   for (int pass = 0; pass < NP; ++pass) {
     const int i = pass * ROWS + rr;
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) ss = fmaf(ov[pass][k], ov[pass][k], ss);
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off, 64);
+      for (int k = 0; k < 4; ++k) ss = fmaf(ov[pass][hf][k], ov[pass][hf][k], ss);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
     if (i < nc) {
       const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0;
-      if constexpr (VPL == 4) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
         f32x4 yv;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) yv[k] = nw[k] * ov[pass][k] * inv * silu_fast(zv[pass][k]);
-        io::store4(p.y, o, yv);
-      } else {
-#pragma unroll
-        for (int k = 0; k < VPL; ++k)
-          io::store(p.y, o + k, nw[k] * ov[pass][k] * inv * silu_fast(zv[pass][k]));
+        for (int k = 0; k < 4; ++k)
+          yv[k] = nw[hf][k] * ov[pass][hf][k] * inv * silu_fast(zv[pass][hf][k]);
+        io::store4(p.y, o + 4 * hf, yv);
       }
     }
   }
