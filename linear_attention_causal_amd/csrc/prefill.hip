@@ -659,20 +659,21 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
   }
 }
 
-// One workgroup per (chunk, sequence, V-head).  W's row factor moves onto
-// Tm (W^T = K^T (Tm diag(beta e^gamma))^T) so W takes k_hat^T straight from
-// the q/k kernel's fragments and no k tile is kept here.
+// One workgroup per (chunk, V-head).  W's row factor beta_j e^{gamma_j} is
+// split between the two sides of W^T = (K^T diag(e^gamma)) (Tm diag(beta))^T:
+// e^gamma scales the k_hat^T fragments from the q/k kernel in registers, so
+// W and U share the one LDS tile Tm diag(beta), and the kernel's 54 KB of LDS
+// leave room for three workgroups per CU.
 template <typename Act, int D, int K>
-__global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int LDL = kL + 4, NTL = kL / 16, NDB = D / 16;
   constexpr int LDH = kL + 8;   // bf16 row length of the split Tm tiles
   static_assert(D * LDL <= 2 * kL * LDL, "v^T fits the A | Tm tile");
-  static_assert(4 * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits a split tile");
+  static_assert(4 * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the split tile");
   __shared__ __attribute__((aligned(16))) float sAT[2 * kL * LDL];   // A | Tm, then v^T
-  __shared__ __attribute__((aligned(16))) __bf16 sTs[2][kL * LDH];   // Tm diag(beta e^gamma)
   __shared__ __attribute__((aligned(16))) __bf16 sTb[2][kL * LDH];   // Tm diag(beta)
-  __shared__ float sGam[kL], sBeta[kL], sSc[kL];
+  __shared__ float sGam[kL], sBeta[kL], sEg[kL];
   float* sA = sAT;
   float* sT = sAT + kL * LDL;
   float* sVt = sAT;
@@ -743,7 +744,7 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
       ktl[it][ks] = ld8(p.s.kt[1] + at);
     }
   }
-  // gates: running sum gamma, beta, and the W row factor beta e^gamma
+  // gates: running sum gamma, beta, and e^gamma (the K side of W's factor)
   if (wave == 0) {
     float gv = 0.f, bv = 0.f;
     if (lane < nc) gates(alog, dtb, a_in, b_in, gv, bv);
@@ -754,7 +755,7 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
     }
     sGam[lane] = gv;
     sBeta[lane] = bv;
-    sSc[lane] = bv * expf(gv);
+    sEg[lane] = expf(gv);
     p.s.gam[gh * kL + lane] = gv;
   }
   __syncthreads();
@@ -784,22 +785,16 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
   float vout[VTPT][VV];
   if (vact) vct.finish(nc, vi_off, vout);   // held until A and Tm are dead
   __syncthreads();
-  unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTs[0][0]), tid);
-  // Tm scaled by the W and U row factors, split (strictly upper blocks zero)
+  // (the inverse stages its blocks in sTb and ends with a barrier)
+  unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTb[0][0]), tid);
+  // Tm diag(beta), split (strictly upper blocks zero)
   for (int u = tid; u < kL * (kL / 8); u += kNT) {
     const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
     const bool upper = (j0 >> 4) > (i >> 4);
-    float vs[8], vb[8];
+    float vb[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = upper ? 0.f : sT[i * LDL + j0 + e];
-      vs[e] = t * sSc[j0 + e];
-      vb[e] = t * sBeta[j0 + e];
-    }
+    for (int e = 0; e < 8; ++e) vb[e] = upper ? 0.f : sT[i * LDL + j0 + e] * sBeta[j0 + e];
     bf16x8 h8, l8;
-    split8(vs, h8, l8);
-    *reinterpret_cast<bf16x8*>(&sTs[0][i * LDH + j0]) = h8;
-    *reinterpret_cast<bf16x8*>(&sTs[1][i * LDH + j0]) = l8;
     split8(vb, h8, l8);
     *reinterpret_cast<bf16x8*>(&sTb[0][i * LDH + j0]) = h8;
     *reinterpret_cast<bf16x8*>(&sTb[1][i * LDH + j0]) = l8;
@@ -816,8 +811,17 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
     const int db = wave + kNW * it;
     if (db >= NDB) break;   // uniform: fewer column blocks than waves
     const int d = 16 * db + li;
-    const bf16x8* kh = kth[it];
-    const bf16x8* kl = ktl[it];
+    // k_hat^T rows d times e^{gamma_j} at token j = 32 ks + 8 lk + e, split
+    // again (A operand of W^T)
+    bf16x8 kh[2], kl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float kv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        kv[e] = ((float)kth[it][ks][e] + (float)ktl[it][ks][e]) * sEg[32 * ks + 8 * lk + e];
+      split8(kv, kh[ks], kl[ks]);
+    }
     // v^T rows d, split (B operand of U)
     bf16x8 vh[2], vl[2];
 #pragma unroll
@@ -829,13 +833,11 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
     }
 #pragma unroll
     for (int tb = 0; tb < NTL; ++tb) {
-      // rows 16 tb + li of the two scaled Tm: B operand of W^T, A operand of U
-      bf16x8 sh[2], sl[2], bh[2], bl[2];
+      // rows 16 tb + li of Tm diag(beta): B operand of W^T and A operand of U
+      bf16x8 bh[2], bl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int o = (16 * tb + li) * LDH + 32 * ks + 8 * lk;
-        sh[ks] = ld8(&sTs[0][o]);
-        sl[ks] = ld8(&sTs[1][o]);
         bh[ks] = ld8(&sTb[0][o]);
         bl[ks] = ld8(&sTb[1][o]);
       }
@@ -843,7 +845,7 @@ __global__ __launch_bounds__(kNT) void prefill_wy_kernel(PrefillParams p) {
       Acc3 au = acc3(f32x4{0.f, 0.f, 0.f, 0.f});   // U: rows token, columns d
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        mfma3(aw, kh[ks], kl[ks], sh[ks], sl[ks]);
+        mfma3(aw, kh[ks], kl[ks], bh[ks], bl[ks]);
         mfma3(au, bh[ks], bl[ks], vh[ks], vl[ks]);
       }
       const f32x4 wt = -fold(aw);   // -W[token 16 tb + li][d 16 db + 4 lk + e]
