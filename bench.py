@@ -189,7 +189,7 @@ def bench_decode(args):
                   "unit": "GB/s", "frac": achieved / HBM_PEAK,
                   "traffic": rec["hbm_bytes_per_launch"] if rec else None,
                   "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
-                  "kernel": "gdn::decode_step_kernel<__bf16, 128, 2, 4>",
+                  "kernel": "gdn::decode_head_kernel<__bf16, 128, 4, 1>",
                   "bytes_per_launch": per_launch, "mean_launch_us": launch_ms * 1e3,
                   "timing": f"HIP events around graph replays of {G} back-to-back launches "
                             f"({GRAPH_PASSES} passes over {R} replicas)"},

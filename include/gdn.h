@@ -164,7 +164,13 @@ int gdn_decode_batch(const gdn_geometry* geom, const gdn_layer_weights* w,
  * batched decode chain of pegainfer issue #1001, Splits, with the conv and
  * the state update of one layer in a single kernel).  Arguments as in those
  * two calls; qkv_in [B][C] act.  Results equal the two-call sequence.
- * Compiled for Hv/Hk in {1, 2, 4}; otherwise GDN_E_UNSUPPORTED. */
+ * One workgroup runs per (row, V-head); the Hv/Hk workgroups that share a
+ * K-head's q/k conv window agree on which of them writes it back through
+ * arrival counters the library keeps per (slot number, K-head, 64 q/k
+ * channels), zero between calls.  Any Hv/Hk is taken while num_slots * Hk *
+ * (2 dk / 64) <= 65536; past that a per-K-head kernel runs, for Hv/Hk in
+ * {1, 2, 4} (otherwise GDN_E_UNSUPPORTED).  Two calls that overlap in time on
+ * one GPU must not name the same slot number, even in different pools. */
 int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
                     const gdn_state_pool* pool, const int32_t* slot_idx,
                     const int32_t* slot_idx_host, int32_t B, const void* qkv_in,

@@ -191,10 +191,12 @@ int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
   GDN_TRY(check_geometry(geom));
   GDN_TRY(check_weights(w));
   GDN_TRY(check_pool(pool, true, true));
-  if (!gdn::decode_step_supported(*geom))
-    return fail(GDN_E_UNSUPPORTED, "fused decode step compiled for Hv/Hk in {1, 2, 4}");
+  if (!gdn::decode_step_supported(*geom, pool->num_slots))
+    return fail(GDN_E_UNSUPPORTED,
+                "fused decode step: Hv/Hk must be 1, 2 or 4 for a pool of %d slots",
+                pool->num_slots);
   if (B < 0) return fail(GDN_E_SHAPE, "B = %d is negative", B);
-  if ((long long)B * geom->num_k_heads > 0x7fffffffLL) return fail(GDN_E_SHAPE, "B too large");
+  if ((long long)B * geom->num_v_heads > (1LL << 30)) return fail(GDN_E_SHAPE, "B too large");
   if (B == 0) return ok();
   if (!slot_idx || !qkv_in || !z || !a || !b || !y)
     return fail(GDN_E_NULL, "a device array is NULL");

@@ -9,6 +9,9 @@
 //                       S[dk][dv], and the gated RMSNorm epilogue (pegainfer
 //                       issue #1001, Splits, "Batched eager TP decode": one
 //                       batched launch over all decode rows).
+//   decode_head_kernel  both in one launch, per (row, V-head) (the fused
+//                       step); decode_step_kernel is its per-K-head form,
+//                       for pools too large for the arrival counters.
 //
 // The state update reads S once: with kappa = S^T k and rho = S^T q taken from
 // the old state,
@@ -253,6 +256,8 @@ struct StepParams {
   const float* dt_bias;
   const float* norm_w;
   int B, Hk, Hv, C, num_slots;
+  int r;                // Hv / Hk
+  int per_xcd;          // (row, V-head) units per XCD lane of the grid
   float l2eps, rmseps, scale;
 };
 
@@ -461,6 +466,287 @@ __global__ __launch_bounds__(kStepThreadsPerDim * D * R) void decode_step_kernel
   }
 }
 
+// Arrival counters of decode_head_kernel: one per (slot, K-head, wave of q/k
+// channels).  Zero between calls.
+constexpr int kArrivalCounters = 1 << 16;
+__device__ unsigned int g_arrivals[kArrivalCounters];
+
+// One workgroup of 2D threads per (row, V-head): twice the workgroups of the
+// per-K-head kernel above, so each CU moves half as many state bytes (the
+// per-CU load path, not HBM, sets a small batch's time).  The r = Hv/Hk
+// workgroups of one (row, K-head) each convolve the K-head's q/k channels
+// from the old conv window; the shifted q/k window may be written only after
+// all r have read it.  Each wave holds 64 q/k channels and, once its loads of
+// them have returned, adds one to the (slot, K-head, wave) counter; the
+// arrival that finds r-1 (mod r) earlier arrivals is the last reader, writes
+// those channels' shifted window and takes r back off the counter.  Nobody
+// waits for anybody.  The v channels of V-head h have one reader, their own
+// workgroup, which writes them back at once.  Block x runs unit
+// (x % 8) * per_xcd + x / 8, which keeps the r units of a (row, K-head) on
+// one XCD (blocks are dealt to the eight XCDs in turn).
+template <typename Act, int D, int K, int NQ>
+__global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
+  using io = act_io<Act>;
+  constexpr int NT = 2 * D;          // threads of the V-head
+  constexpr int CW = D / NQ;         // columns per chunk
+  constexpr int CGH = CW / 4;        // four-column groups per chunk
+  constexpr int RG = NT / CGH;       // row groups
+  constexpr int RPT = D / RG;        // rows per thread per chunk
+  constexpr int HW = NT / 64;        // waves (each holds 64 of the 2D q/k channels)
+  static_assert(NT % 64 == 0 && CGH <= 64 && 64 % CGH == 0 && RPT >= 1, "layout");
+
+  __shared__ float s_x[3 * D];       // conv + SiLU output: q, k, v_h
+  __shared__ f32x4 s_red[NQ][HW][2][CGH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cgh = tid % CGH, rg = tid / CGH;
+  const int unit = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+  if (unit >= p.B * p.Hv) return;
+  const int row = unit / p.Hv;
+  const int h = unit - row * p.Hv;
+  const int m = h / p.r;
+  const size_t out_off = ((size_t)row * p.Hv + h) * D;
+  const int slot = p.slot_idx[row];
+  if (slot < 0 || slot >= p.num_slots) {  // padding row: zeros, no state access
+    if (tid < D) {
+      io::store(p.y, out_off + tid, 0.f);
+      if (p.o_raw) p.o_raw[out_off + tid] = 0.f;
+    }
+    return;
+  }
+
+  // 1. conv inputs (window columns 1..K-1, the token, the weights), then the
+  // tile.  Thread t holds q/k channel t of [q_m | k_m] and, for t < D, v
+  // channel t of V-head h (loads from a clamped channel, so unconditional).
+  // The small inputs stay unconverted until the tile's loads are out (a
+  // conversion scheduled among those loads would wait for its own).
+  void* win = static_cast<char*>(p.conv) + (size_t)slot * K * p.C * io::bytes;
+  const int chq = tid < D ? m * D + tid : (p.Hk + m) * D + tid - D;
+  const int chv = 2 * p.Hk * D + h * D + (tid < D ? tid : D - 1);
+  typename io::raw_t rcq[K], rwq[K], rcv[K], rwv[K];
+#pragma unroll
+  for (int k = 1; k < K; ++k) {
+    rcq[k - 1] = io::load_raw(win, (size_t)k * p.C + chq);
+    rcv[k - 1] = io::load_raw(win, (size_t)k * p.C + chv);
+  }
+  rcq[K - 1] = io::load_raw(p.x, (size_t)row * p.C + chq);
+  rcv[K - 1] = io::load_raw(p.x, (size_t)row * p.C + chv);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    rwq[k] = io::load_raw(p.weight, (size_t)chq * K + k);
+    rwv[k] = io::load_raw(p.weight, (size_t)chv * K + k);
+  }
+  const typename io::raw_t ra = io::load_raw(p.a, (size_t)row * p.Hv + h);
+  const typename io::raw_t rb = io::load_raw(p.b, (size_t)row * p.Hv + h);
+  const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
+  // the epilogue's z and norm weight too (every thread, its four columns),
+  // so the end of the kernel waits on no load
+  typename io::raw4_t rz[NQ];
+  f32x4 nw[NQ];
+#pragma unroll
+  for (int hf = 0; hf < NQ; ++hf) {
+    rz[hf] = io::load4_raw(p.z, out_off + hf * CW + 4 * cgh);
+    nw[hf] = *reinterpret_cast<const f32x4*>(p.norm_w + hf * CW + 4 * cgh);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
+  // issued in the order the reduction consumes them (the scheduler otherwise
+  // reverses it and the first product waits for the whole tile); nothing
+  // moves across the barriers
+  f32x4 s[NQ][RPT];
+#pragma unroll
+  for (int hf = 0; hf < NQ; ++hf)
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      s[hf][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+          S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  float cq[K], wq[K], cv[K], wv[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    cq[k] = io::from_raw(rcq[k]);
+    cv[k] = io::from_raw(rcv[k]);
+    wq[k] = io::from_raw(rwq[k]);
+    wv[k] = io::from_raw(rwv[k]);
+  }
+  const float a_in = io::from_raw(ra), b_in = io::from_raw(rb);
+  f32x4 zz[NQ];
+#pragma unroll
+  for (int hf = 0; hf < NQ; ++hf) zz[hf] = io::from_raw4(rz[hf]);
+
+  // 2. conv + SiLU
+  float accq = 0.f, accv = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    accq = fmaf(wq[k], cq[k], accq);
+    accv = fmaf(wv[k], cv[k], accv);
+  }
+  s_x[tid] = silu(accq);
+  if (tid < D) s_x[2 * D + tid] = silu(accv);
+  // The v window is written back by every thread (those past D repeat
+  // channel D-1 with its own values): stores under a branch between the
+  // tile's loads and their use would make the reduction wait for all of them
+  // at once instead of load by load.
+#pragma unroll
+  for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chv, cv[k]);
+  // arrival (lane 0 of each wave; one atomic per wave); the increment takes
+  // accq as an operand (through an empty asm), so it issues only after this
+  // wave's q/k window loads have returned
+  const size_t ctr = ((size_t)slot * p.Hk + m) * HW + wave;
+  unsigned int arrived = 0;
+  unsigned int one = 1;
+  asm volatile("" : "+v"(one) : "v"(accq));
+  if (lane == 0 && p.r > 1)
+    arrived = __hip_atomic_fetch_add(&g_arrivals[ctr], one, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  float g, beta;
+  gates(A_log, dt_bias, a_in, b_in, g, beta);
+  const float eg = expf(g);
+  __syncthreads();
+
+  const float* sq = s_x;
+  const float* sk = s_x + D;
+  const float* sv = s_x + 2 * D;
+  float sqq = 0.f, skk = 0.f, sqk = 0.f;
+  for (int j = lane; j < D; j += 64) {
+    const float qv = sq[j], kv = sk[j];
+    sqq = fmaf(qv, qv, sqq);
+    skk = fmaf(kv, kv, skk);
+    sqk = fmaf(qv, kv, sqk);
+  }
+  sqq = wave_sum(sqq);
+  skk = wave_sum(skk);
+  sqk = wave_sum(sqk);
+  const float rq = p.scale / sqrtf(sqq + p.l2eps);
+  const float rk = 1.0f / sqrtf(skk + p.l2eps);
+  const float kq = sqk * rq * rk;
+  float kr[RPT], qr[RPT];   // k_hat, q_hat at this thread's rows
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    kr[i] = sk[rg + RG * i] * rk;
+    qr[i] = sq[rg + RG * i] * rq;
+  }
+
+  // 3. per column chunk (a chunk's columns need only its own loads): reduce
+  // (kappa = S^T k, rho = S^T q), update, store
+  f32x4 o[NQ];
+#pragma unroll
+  for (int hf = 0; hf < NQ; ++hf) {
+    f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      kap += s[hf][i] * kr[i];
+      rho += s[hf][i] * qr[i];
+    }
+#pragma unroll
+    for (int off = CGH; off < 64; off <<= 1) {
+      kap.x += __shfl_xor(kap.x, off, 64); kap.y += __shfl_xor(kap.y, off, 64);
+      kap.z += __shfl_xor(kap.z, off, 64); kap.w += __shfl_xor(kap.w, off, 64);
+      rho.x += __shfl_xor(rho.x, off, 64); rho.y += __shfl_xor(rho.y, off, 64);
+      rho.z += __shfl_xor(rho.z, off, 64); rho.w += __shfl_xor(rho.w, off, 64);
+    }
+    if (lane < CGH) {
+      s_red[hf][wave][0][cgh] = kap;
+      s_red[hf][wave][1][cgh] = rho;
+    }
+    __syncthreads();
+    kap = s_red[hf][0][0][cgh];
+    rho = s_red[hf][0][1][cgh];
+#pragma unroll
+    for (int w = 1; w < HW; ++w) {
+      kap += s_red[hf][w][0][cgh];
+      rho += s_red[hf][w][1][cgh];
+    }
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[hf * CW + 4 * cgh]);
+    const f32x4 u = beta * (v - eg * kap);
+    o[hf] = eg * rho + u * kq;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      f32x4 ns;
+      ns.x = fmaf(eg, s[hf][i].x, kr[i] * u.x);
+      ns.y = fmaf(eg, s[hf][i].y, kr[i] * u.y);
+      ns.z = fmaf(eg, s[hf][i].z, kr[i] * u.z);
+      ns.w = fmaf(eg, s[hf][i].w, kr[i] * u.w);
+      __builtin_nontemporal_store(
+          ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
+    }
+  }
+
+  // 4. gated RMSNorm over the D outputs (first wave; each row group holds all
+  // columns, so the xor-reduction over its CGH lanes gives the full sum)
+  if (wave == 0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < NQ; ++hf)
+      ss += o[hf].x * o[hf].x + o[hf].y * o[hf].y + o[hf].z * o[hf].z + o[hf].w * o[hf].w;
+#pragma unroll
+    for (int off = 1; off < CGH; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
+    if (lane < CGH) {
+#pragma unroll
+      for (int hf = 0; hf < NQ; ++hf) {
+        const int c0 = hf * CW + 4 * cgh;
+        f32x4 yv;
+        yv.x = nw[hf].x * o[hf].x * inv * silu(zz[hf].x);
+        yv.y = nw[hf].y * o[hf].y * inv * silu(zz[hf].y);
+        yv.z = nw[hf].z * o[hf].z * inv * silu(zz[hf].z);
+        yv.w = nw[hf].w * o[hf].w * inv * silu(zz[hf].w);
+        io::store4(p.y, out_off + c0, yv);
+        if (p.o_raw) *reinterpret_cast<f32x4*>(p.o_raw + out_off + c0) = o[hf];
+      }
+    }
+  }
+
+  // 5. the last reader of this wave's q/k channels writes their shifted window
+  bool last = true;
+  if (p.r > 1) {
+    const unsigned int before = __builtin_amdgcn_readfirstlane(arrived);
+    last = before % (unsigned int)p.r == (unsigned int)(p.r - 1);
+  }
+  if (last) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chq, cq[k]);
+    if (p.r > 1 && lane == 0)
+      __hip_atomic_fetch_add(&g_arrivals[ctr], 0u - (unsigned int)p.r, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+constexpr int kHeadChunks = 1;   // column chunks of the state tile (NQ)
+
+template <typename Act, int D>
+static hipError_t head_k(const StepParams& p, int K, hipStream_t st) {
+  dim3 grid(8 * p.per_xcd);
+  constexpr int NQ = kHeadChunks;
+  switch (K) {
+    case 2: decode_head_kernel<Act, D, 2, NQ><<<grid, 2 * D, 0, st>>>(p); break;
+    case 3: decode_head_kernel<Act, D, 3, NQ><<<grid, 2 * D, 0, st>>>(p); break;
+    case 4: decode_head_kernel<Act, D, 4, NQ><<<grid, 2 * D, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename Act>
+static hipError_t head_d(const StepParams& p, int D, int K, hipStream_t st) {
+  switch (D) {
+    case 32: return head_k<Act, 32>(p, K, st);
+    case 64: return head_k<Act, 64>(p, K, st);
+    case 128: return head_k<Act, 128>(p, K, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The per-V-head kernel runs when its counters cover the pool's slots (or
+// when no K-head is shared); otherwise the per-K-head kernel.
+static bool use_head_kernel(const gdn_geometry& g, int num_slots) {
+  const int r = g.num_v_heads / g.num_k_heads;
+  const long long waves = 2LL * g.head_k_dim / 64;
+  return r == 1 || (long long)num_slots * g.num_k_heads * waves <= kArrivalCounters;
+}
+
 template <typename Act, int D, int R>
 static hipError_t step_k(const StepParams& p, int K, hipStream_t st) {
   dim3 grid(p.B * p.Hk);
@@ -494,9 +780,9 @@ static hipError_t step_d(const StepParams& p, int D, int R, int K, hipStream_t s
   }
 }
 
-bool decode_step_supported(const gdn_geometry& g) {
+bool decode_step_supported(const gdn_geometry& g, int num_slots) {
   const int r = g.num_v_heads / g.num_k_heads;
-  return r == 1 || r == 2 || r == 4;
+  return use_head_kernel(g, num_slots) || r == 2 || r == 4;
 }
 
 hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
@@ -526,6 +812,15 @@ hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
   p.rmseps = g.rmsnorm_eps;
   p.scale = g.scale > 0.f ? g.scale : 1.0f / sqrtf((float)g.head_k_dim);
   const int R = g.num_v_heads / g.num_k_heads;
+  p.r = R;
+  if (use_head_kernel(g, pool.num_slots)) {
+    const int units = B * p.Hv;
+    const int per = (units + 7) / 8;
+    p.per_xcd = (per + R - 1) / R * R;   // a (row, K-head) never straddles two XCDs
+    if (g.act_dtype == GDN_BF16) return head_d<__bf16>(p, g.head_k_dim, g.conv_kernel, stream);
+    return head_d<float>(p, g.head_k_dim, g.conv_kernel, stream);
+  }
+  p.per_xcd = 0;
   if (g.act_dtype == GDN_BF16) return step_d<__bf16>(p, g.head_k_dim, R, g.conv_kernel, stream);
   return step_d<float>(p, g.head_k_dim, R, g.conv_kernel, stream);
 }

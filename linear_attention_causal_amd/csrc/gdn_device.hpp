@@ -36,6 +36,9 @@ template <> struct act_io<float> {
     return static_cast<const float*>(p)[i];
   }
   static __device__ __forceinline__ float from_raw(raw_t r) { return r; }
+  using raw4_t = f32x4;
+  static __device__ __forceinline__ raw4_t load4_raw(const void* p, size_t i) { return load4(p, i); }
+  static __device__ __forceinline__ f32x4 from_raw4(raw4_t r) { return r; }
   static constexpr int bytes = 4;
 };
 
@@ -76,6 +79,18 @@ template <> struct act_io<__bf16> {
     return static_cast<const unsigned short*>(p)[i];
   }
   static __device__ __forceinline__ float from_raw(raw_t r) { return bf16_bits_to_f32(r); }
+  using raw4_t = uint2;
+  static __device__ __forceinline__ raw4_t load4_raw(const void* p, size_t i) {
+    return *reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(p) + i);
+  }
+  static __device__ __forceinline__ f32x4 from_raw4(raw4_t u) {
+    f32x4 r;
+    r.x = __uint_as_float(u.x << 16);
+    r.y = __uint_as_float(u.x & 0xffff0000u);
+    r.z = __uint_as_float(u.y << 16);
+    r.w = __uint_as_float(u.y & 0xffff0000u);
+    return r;
+  }
   static constexpr int bytes = 2;
 };
 

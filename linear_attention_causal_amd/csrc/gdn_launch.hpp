@@ -18,7 +18,7 @@ hipError_t launch_decode(const gdn_geometry& g, const gdn_layer_weights& w,
                          const float* qkv, const void* z, const void* a,
                          const void* b, void* y, float* o_raw, hipStream_t stream);
 
-bool decode_step_supported(const gdn_geometry& g);
+bool decode_step_supported(const gdn_geometry& g, int num_slots);
 
 hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
                               const gdn_state_pool& pool, const int32_t* slot_idx, int B,

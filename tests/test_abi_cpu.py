@@ -123,6 +123,22 @@ def test_decode_batch_checks():
     assert _decode(slots_host=h) == _abi.GDN_E_SLOT
 
 
+def test_decode_step_head_ratio_checks():
+    """gdn_decode_step takes any Hv/Hk while its per-(slot, K-head) arrival
+    counters cover the pool; past that it falls back to the per-K-head kernel,
+    which exists for Hv/Hk in {1, 2, 4}.  B = 0 returns before any launch."""
+    def step(g, P, B=0):
+        w, p = weights(), pool(P)
+        return lib.gdn_decode_step(ctypes.byref(g), ctypes.byref(w), ctypes.byref(p), DEV, None,
+                                   B, DEV, DEV, DEV, DEV, DEV, None, None)
+    g3 = geom(Hk=2, Hv=6, d=32)          # one wave of q/k channels per K-head
+    assert step(g3, P=32768) == 0        # 2 * 32768 counters: covered
+    assert step(g3, P=32769) == _abi.GDN_E_UNSUPPORTED
+    assert step(geom(Hk=2, Hv=4, d=32), P=1 << 20) == 0    # falls back
+    assert step(geom(Hk=16, Hv=16), P=1 << 20) == 0        # r = 1 needs no counter
+    assert step(geom(Hk=2, Hv=4, d=32), P=64, B=-1) == _abi.GDN_E_SHAPE
+
+
 def _prefill(cu, slots_host=None, scratch=DEV, nbytes=1 << 40, N=None):
     g, w, p = geom(), weights(), pool()
     cu_a, cu_p = host_i32(cu)
