@@ -14,8 +14,8 @@
 //     waves split K and request every weight and input fragment of their K
 //     range before the first MFMA, and add their partial tiles through LDS.
 //   tile (M > 32): a dense product.  A workgroup owns a BM x BN output tile
-//     (the largest of 128 x 128, 128 x 64, 64 x 64 that still gives 128
-//     workgroups); x and w tiles of 32 k-columns are staged through three
+//     (the largest of 128 x 128 (eight waves), 128 x 64, 64 x 64 (four) that
+//     still gives 128 workgroups); x and w tiles of 32 k-columns are staged through three
 //     LDS buffers in MFMA fragment order, so each wave reads its operands
 //     with linear 16-byte LDS reads, and the input rows are fetched once
 //     per BN columns instead of once per 16.  Global loads run eight
@@ -139,16 +139,22 @@ __global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
   }
 }
 
-// BM x BN output tile, four waves as 2 x 2, each wave (BM/2) x (BN/2).
+// BM x BN output tile, NW waves as 2 x NW/2, each wave (BM/2) x (2 BN/NW).
+// The 128 x 128 tile runs eight waves (two per SIMD, so one wave's LDS and
+// barrier waits overlap the other's MFMAs); with four, each wave's registers
+// allow only one wave per SIMD.
 // Global loads run D k-steps ahead of the MFMAs through a ring of D
 // register stages; each k-step is copied into one of three LDS buffers two
 // steps before its MFMAs, and its fragments are read from LDS one step
 // before, so LDS latency hides behind the previous step's MFMAs.
-template <int BM, int BN, int D>
-__global__ __launch_bounds__(256) void linear_tile_kernel(LinParams p) {
+template <int BM, int BN, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
   static_assert(D >= 3, "the ring holds the two k-steps ahead of the LDS copy");
-  constexpr int TM = BM / 32, TN = BN / 32;         // 16 x 16 tiles per wave
-  constexpr int XP = BM / 64, WP = BN / 64;         // 16-byte pieces per thread per k-step
+  constexpr int NTH = 64 * NW;                      // threads
+  constexpr int WNW = NW / 2;                       // waves along n (two along m)
+  constexpr int TM = BM / 32, TN = BN / (16 * WNW); // 16 x 16 tiles per wave
+  constexpr int XP = 4 * BM / NTH, WP = 4 * BN / NTH; // 16-byte pieces per thread per k-step
+  static_assert(TN >= 1 && XP >= 1 && WP >= 1, "tile shape");
   // one k-step of each operand in fragment order: [16-row tile][lane] x 16 bytes
   __shared__ lbf16x8 xs[3][BM / 16][64];
   __shared__ lbf16x8 ws[3][BN / 16][64];
@@ -156,9 +162,9 @@ __global__ __launch_bounds__(256) void linear_tile_kernel(LinParams p) {
   const LinearOut o = p.out[g];
   const int n0 = ((int)blockIdx.x - o.tile0) * BN, m0 = blockIdx.y * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int ksteps = (p.K + 31) / 32;
-  // piece q = tid + 256 i: tile row r = q / 4, k-chunk c = q % 4 (the same c
+  // piece q = tid + NTH i: tile row r = q / 4, k-chunk c = q % 4 (the same c
   // for every piece of a thread); its LDS slot is fragment r / 16, lane
   // r % 16 + 16 c.  Rows past M or N are clamped (read, never stored); a
   // k-chunk past K reads the row start, and the MFMAs zero it (a select on
@@ -170,13 +176,13 @@ __global__ __launch_bounds__(256) void linear_tile_kernel(LinParams p) {
   int xslot[XP], wslot[WP];
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
-    const int r = (tid + 256 * i) >> 2;
+    const int r = (tid + NTH * i) >> 2;
     xsrc[i] = p.x + (size_t)min(m0 + r, p.M - 1) * p.ldx;
     xslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
   }
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
-    const int r = (tid + 256 * i) >> 2;
+    const int r = (tid + NTH * i) >> 2;
     wsrc[i] = o.w + (size_t)min(n0 + r, o.N - 1) * p.K;
     wslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
   }
@@ -316,10 +322,10 @@ hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* 
     return launch(linear_stream_kernel<2, 2, 4>, p, outs, 32, 32, 256, stream);
   }
   if (plan.rows == 128 && plan.cols == 128)
-    return launch(linear_tile_kernel<128, 128, 8>, p, outs, 128, 128, 256, stream);
+    return launch(linear_tile_kernel<128, 128, 8, 8>, p, outs, 128, 128, 512, stream);
   if (plan.rows == 128)
-    return launch(linear_tile_kernel<128, 64, 8>, p, outs, 64, 128, 256, stream);
-  return launch(linear_tile_kernel<64, 64, 8>, p, outs, 64, 64, 256, stream);
+    return launch(linear_tile_kernel<128, 64, 8, 4>, p, outs, 64, 128, 256, stream);
+  return launch(linear_tile_kernel<64, 64, 8, 4>, p, outs, 64, 64, 256, stream);
 }
 
 }  // namespace gdn

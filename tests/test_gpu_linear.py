@@ -56,6 +56,7 @@ def _run_linear(M, K, Ns, seed, x_pad=0, y_pad=0):
     (64, 200, [40, 8]),                   # tiled, K not a multiple of 32
     (130, 72, [200, 5]),                  # tiled, partial row block and K tail
     (512, 1024, [1024]),                  # tiled, large tile
+    (300, 200, [16000, 7]),               # 128 x 128 tile: partial row tile, K tail, ragged N
 ])
 def test_linear(M, K, Ns):
     _run_linear(M, K, Ns, seed=M + K)
