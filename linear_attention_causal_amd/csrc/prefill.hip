@@ -34,7 +34,8 @@
 //             state carry on one half of the waves, O = e^gamma Q S + P V' on
 //             the other half, on 3-pass bf16 MFMA (x = hi + lo; hi*hi + hi*lo
 //             + lo*hi with f32 accumulation, about 2^-16 relative), O
-//             (pre-norm) to f32.
+//             (pre-norm) to the caller's f32 o_raw, or to a bf16 copy in the
+//             scratch when a bf16 layer is called without one.
 //   3. norm   (chunk, V-head): gated RMSNorm with SiLU(z) -> y.
 // The per-chunk launches (1, 1', 3) cover the real chunks of the batch when
 // the prefix travels with the launch, else every (chunk slot, sequence) pair
@@ -131,6 +132,10 @@ struct PrefillParams {
   const void* b;        // [T][Hv] act
   void* y;              // [T][Hv][D] act
   float* obuf;          // [T][Hv][D] f32: caller's o_raw or scratch
+  // Pre-norm output kept as bf16 in the scratch (bf16 layers called without
+  // o_raw): it feeds only the gated RMSNorm, whose bf16 result it perturbs
+  // by at most about 2^-8 relative; the state path is unaffected.
+  bool o_bf16;
   float* rec;           // [P][Hv][D][D]
   void* conv;           // [P][K][C] act
   const int32_t* cu;    // [N+1]
@@ -888,7 +893,7 @@ struct ChunkOps {
 // the same S and V' tiles in LDS, beside it, so the serial chain per chunk
 // is two contractions and two barriers.  Every operand fetch is one
 // contiguous 1 KB fragment block per wave.
-template <typename Act, int D, int K, int NCB>
+template <typename Act, int D, int K, int NCB, bool OB>
 __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int DVT = 16 * NCB;        // state columns of the workgroup
@@ -1110,7 +1115,11 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = i0 + e;
-            if (i < nc) p.obuf[((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li] = o[e];
+            const size_t at = ((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li;
+            if (i < nc) {
+              if constexpr (OB) reinterpret_cast<__bf16*>(p.obuf)[at] = static_cast<__bf16>(o[e]);
+              else p.obuf[at] = o[e];
+            }
           }
         }
       }
@@ -1165,7 +1174,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
 // bf16, 32 bytes of the f32 pre-norm output).  Every load of the chunk (rows
 // clamped to the chunk so no load is conditional) is requested before any
 // arithmetic.
-template <typename Act, int D>
+template <typename Act, int D, bool OB>
 __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int VPL = 8;           // values per lane
@@ -1191,7 +1200,7 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
         for (int k = 0; k < VPL; ++k) {
           const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0 + k;
           io::store(p.y, o, 0.f);
-          p.obuf[o] = 0.f;
+          if (!OB) p.obuf[o] = 0.f;   // (the bf16 scratch copy is no output)
         }
     }
     return;
@@ -1201,11 +1210,19 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   for (int pass = 0; pass < NP; ++pass) {
     const int i = min(pass * ROWS + rr, nc - 1);
     const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0;
+    if constexpr (OB) {
+      const bf16x8 ob = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.obuf) + o);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      ov[pass][hf] = *reinterpret_cast<const f32x4*>(p.obuf + o + 4 * hf);
-      zv[pass][hf] = io::load4(p.z, o + 4 * hf);
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ov[pass][hf][k] = static_cast<float>(ob[4 * hf + k]);
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        ov[pass][hf] = *reinterpret_cast<const f32x4*>(p.obuf + o + 4 * hf);
     }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) zv[pass][hf] = io::load4(p.z, o + 4 * hf);
   }
   f32x4 nw[2];
 #pragma unroll
@@ -1252,7 +1269,11 @@ static void launch_state(const PrefillParams& p, hipStream_t st) {
   // groups of 8 (sequence, K-head) units, each unit r * tiles workgroups
   const long long units = (long long)p.N * p.Hk, per = (long long)p.r * (D / (16 * NCB));
   const long long groups = (units + 7) / 8;
-  prefill_state_kernel<Act, D, K, NCB><<<dim3((unsigned)(groups * 8 * per)), kSNT, 0, st>>>(p);
+  const dim3 grid((unsigned)(groups * 8 * per));
+  if (p.o_bf16)
+    prefill_state_kernel<Act, D, K, NCB, true><<<grid, kSNT, 0, st>>>(p);
+  else
+    prefill_state_kernel<Act, D, K, NCB, false><<<grid, kSNT, 0, st>>>(p);
 }
 
 template <typename Act, int D, int K>
@@ -1271,8 +1292,12 @@ static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_
     case 4: if constexpr (D >= 64) launch_state<Act, D, K, 4>(p, st); break;
     default: return hipErrorInvalidValue;
   }
-  if (max_chunks > 0)
-    prefill_norm_kernel<Act, D><<<dim3(chunks.x, chunks.y, p.Hv), kNT, 0, st>>>(p);
+  if (max_chunks > 0) {
+    if (p.o_bf16)
+      prefill_norm_kernel<Act, D, true><<<dim3(chunks.x, chunks.y, p.Hv), kNT, 0, st>>>(p);
+    else
+      prefill_norm_kernel<Act, D, false><<<dim3(chunks.x, chunks.y, p.Hv), kNT, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
@@ -1330,6 +1355,7 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
     }
   }
   p.obuf = o_raw ? o_raw : p.s.o;
+  p.o_bf16 = !o_raw && g.act_dtype == GDN_BF16;
   p.T = total_tokens;
   p.N = N;
   p.Hk = g.num_k_heads;

@@ -213,3 +213,38 @@ def test_prefill_equals_decode_steps():
     assert_close("y", maxrel_heads(host(ya), np.concatenate(ys)), y_tol(s))
     assert_close("state", maxrel_states(host(Pa.rec)[1], host(Pb.rec)[1]), TOL_F32)
     np.testing.assert_array_equal(host(Pa.conv), host(Pb.conv))
+
+
+@pytest.mark.parametrize("case", ["packed", "t4096"])
+def test_prefill_without_o_raw(case):
+    """The call without o_raw, as a serving caller makes it (the pre-norm
+    output then stays internal): y, states and conv windows against the
+    oracle, padding rows zero, untouched slots unchanged."""
+    if case == "packed":
+        s = wl.RANK_LOCAL
+        w, rec, conv, cu, d = _packed(700, s, [70, 1, 200, 64, 129], 8)
+        slots, has_init = [5, 0, -1, 2, 7], [1, 1, 1, 0, 1]
+    else:
+        work = wl.prefill_single(seed=0)
+        s, d = work.shape, work.data
+        w, rec, conv, cu = d["weights"], d["rec"], d["conv"], d["cu_seqlens"]
+        slots, has_init = d["slot_idx"], d["has_init"]
+    print(f"[prefill without o_raw] {case} T={int(cu[-1])}", flush=True)
+    L = Layer(s, w)
+    P = Pool(s, rec, conv)
+    y, _ = prefill(L, P, cu, slots, d["x"], d["z"], d["a"], d["b"], has_init=has_init,
+                   want_o=False)
+    torch.cuda.synchronize()
+    yo, _, S, W = _oracle_prefill(L, rec, conv, cu, slots, d, np.asarray(has_init, np.uint8))
+    yh = host(y)
+    live = np.asarray([sl for sl in slots if sl >= 0])
+    tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
+                          if slots[n] >= 0]).astype(np.int64)
+    assert_close("y", maxrel_heads(yh[tok], yo[tok]), y_tol(s))
+    assert_close("state", maxrel_states(host(P.rec)[live], S[live]), TOL_F32)
+    np.testing.assert_array_equal(host(P.conv)[live], W[live])
+    pad = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
+                          if slots[n] < 0] + [np.zeros(0, np.int64)]).astype(np.int64)
+    assert not yh[pad].any()
+    untouched = np.setdiff1d(np.arange(rec.shape[0]), live)
+    np.testing.assert_array_equal(host(P.rec)[untouched], rec[untouched])
