@@ -184,7 +184,8 @@ int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
  * Description: GdrChunkwiseScratch35).  Sequence n owns tokens
  * [cu_seqlens[n], cu_seqlens[n+1]) of qkv_in [T][C] act, z [T][Hv][dv] act,
  * a, b [T][Hv] act, y [T][Hv][dv] act, o_raw [T][Hv][dv] f32 (or NULL; a bf16
- * layer called without it rounds the pre-norm output it norms to bf16).
+ * layer called without it computes the output side, Q S + P V' and the
+ * pre-norm output it norms, at bf16 precision; the state path is unchanged).
  * It starts from slot slot_idx[n]'s recurrent state and conv window, or from
  * zeros when has_init is given and has_init[n] == 0, and writes its final
  * state and window back to that slot.  Results equal running the tokens one

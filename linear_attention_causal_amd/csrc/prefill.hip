@@ -132,9 +132,11 @@ struct PrefillParams {
   const void* b;        // [T][Hv] act
   void* y;              // [T][Hv][D] act
   float* obuf;          // [T][Hv][D] f32: caller's o_raw or scratch
-  // Pre-norm output kept as bf16 in the scratch (bf16 layers called without
-  // o_raw): it feeds only the gated RMSNorm, whose bf16 result it perturbs
-  // by at most about 2^-8 relative; the state path is unaffected.
+  // bf16 layers called without o_raw: the output-only products (Q S and
+  // P V') run single-pass on the hi halves and the pre-norm output is kept
+  // as bf16 in the scratch; it feeds only the gated RMSNorm, whose bf16
+  // result it perturbs by a few 2^-9 relative.  The state path (W S, the
+  // state update, and everything that feeds them) stays 3-pass.
   bool o_bf16;
   float* rec;           // [P][Hv][D][D]
   void* conv;           // [P][K][C] act
@@ -621,7 +623,7 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
     split8(v, h, l);
     const size_t at = frag_at(gk, kL, D, i, d0);
     *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
-    *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;
+    if (!p.o_bf16) *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;   // (read by 3-pass outputs only)
   }
   for (int u = tid; u < D * (kL / 8); u += kNT) {
     const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
@@ -785,7 +787,7 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
     split8(v, h8, l8);
     const size_t at = frag_at(gh, kL, kL, i, j0);
     *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
-    *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;
+    if (!p.o_bf16) *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;   // (read by 3-pass outputs only)
   }
   float vout[VTPT][VV];
   if (vact) vct.finish(nc, vi_off, vout);   // held until A and Tm are dead
@@ -995,7 +997,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       for (int ks = 0; ks < NKS; ++ks) {
         const size_t at = frag_lane(mat * (4 * NKS) + w4 * NKS + ks, lane);
         ops.fa[ks][0] = ld8(hi + at);
-        ops.fa[ks][1] = ld8(lo + at);
+        if constexpr (REC || !OB) ops.fa[ks][1] = ld8(lo + at);
       }
     };
     auto load_fb = [&](int c) {
@@ -1010,7 +1012,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
         for (int ks = 0; ks < 2; ++ks) {
           const size_t at = frag_lane(blk0 + ks, lane);
           ops.fb[q][ks][0] = ld8(hi + at);
-          ops.fb[q][ks][1] = ld8(lo + at);
+          if constexpr (REC || !OB) ops.fb[q][ks][1] = ld8(lo + at);
         }
       }
     };
@@ -1050,13 +1052,22 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       f32x4 O[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        Acc3 acc = acc3(REC ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 r1;
+        if constexpr (!REC && OB) {
+          // output-only product, single pass (bf16 output path)
+          r1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
-          mfma3(acc, ops.fa[ks][0], ops.fa[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]));
+          for (int ks = 0; ks < NKS; ++ks)
+            r1 = mfma_bf16(ops.fa[ks][0], ld8(&sS[0][(16 * cb + li) * LS + 32 * ks + 8 * lk]), r1);
+        } else {
+          Acc3 acc = acc3(REC ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
+            mfma3(acc, ops.fa[ks][0], ops.fa[ks][1], ld8(&sS[0][bo]), ld8(&sS[1][bo]));
+          }
+          r1 = fold(acc);
         }
-        const f32x4 r1 = fold(acc);
         if constexpr (REC) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -1105,13 +1116,21 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
         // O += P V', stored as the pre-norm output
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          Acc3 ao = acc3(O[cb]);
+          f32x4 o;
+          if constexpr (OB) {
+            o = O[cb];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
-            mfma3(ao, ops.fb[0][ks][0], ops.fb[0][ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]));
+            for (int ks = 0; ks < 2; ++ks)
+              o = mfma_bf16(ops.fb[0][ks][0], ld8(&sV[0][(16 * cb + li) * LR + 32 * ks + 8 * lk]), o);
+          } else {
+            Acc3 ao = acc3(O[cb]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const int bo = (16 * cb + li) * LR + 32 * ks + 8 * lk;
+              mfma3(ao, ops.fb[0][ks][0], ops.fb[0][ks][1], ld8(&sV[0][bo]), ld8(&sV[1][bo]));
+            }
+            o = fold(ao);
           }
-          const f32x4 o = fold(ao);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = i0 + e;
