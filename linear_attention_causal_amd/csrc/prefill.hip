@@ -867,11 +867,16 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------------ 2. state
 
-constexpr int kSW = 8;             // waves of the state kernel
-constexpr int kSNT = 64 * kSW;
+// Recurrence waves of the state kernel: eight for a 16-column tile (one
+// state row block each, half of them idle in the first phase), four
+// otherwise (two row blocks each); four output waves beside them.
+template <int NCB> constexpr int state_rec_waves() { return NCB == 1 ? 8 : 4; }
+template <int NCB> constexpr int state_threads() { return 64 * (state_rec_waves<NCB>() + 4); }
 
-// Compile-time wave role of the state kernel's chunk loop.
-template <bool B> struct WaveRole { static constexpr bool value = B; };
+// Compile-time wave role of the state kernel's chunk loop: 0 recurrence
+// waves that also form V' (token block = wave), 1 recurrence waves that only
+// update their state row blocks, 2 output waves.
+template <int R> struct WaveRole { static constexpr int value = R; };
 
 // Operands of one chunk held in registers by one wave of the state kernel;
 // the next chunk's are fetched into the same registers right after their
@@ -896,17 +901,24 @@ struct ChunkOps {
 // is two contractions and two barriers.  Every operand fetch is one
 // contiguous 1 KB fragment block per wave.
 template <typename Act, int D, int K, int NCB, bool OB>
-__global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
+__global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(PrefillParams p) {
   using io = act_io<Act>;
+  constexpr int NRW = state_rec_waves<NCB>();
+  constexpr int NTH = state_threads<NCB>();
   constexpr int DVT = 16 * NCB;        // state columns of the workgroup
   constexpr int NKS = D / 32;          // k-steps over d
   constexpr int NRB = D / 16;          // 16-row blocks of the state tile
-  constexpr int RBW = (NRB + 3) / 4;   // state row blocks per recurrence wave
+  constexpr int RBW = (NRB + NRW - 1) / NRW;   // state row blocks per recurrence wave
   constexpr int LS = D + 8;            // row length of the transposed state [j][d]
   constexpr int LR = kL + 8;           // row length of [j][token] tiles
   __shared__ __attribute__((aligned(16))) __bf16 sS[2][DVT * LS];   // S_c, B operand
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][DVT * LR];   // V'
   __shared__ __attribute__((aligned(16))) __bf16 sD[2][DVT * LR];   // e^{gamma_L - gamma} V'
+  // bf16 outputs with eight recurrence waves: the output waves leave a
+  // chunk's O here and the state-only recurrence waves, idle in the next
+  // chunk's first phase, write it out with 16-byte stores
+  constexpr bool STAGE_O = OB && NRW == 8;
+  __shared__ __attribute__((aligned(16))) __bf16 sO[STAGE_O ? kL * DVT : 8];
 
   // Workgroup id -> (sequence, V-head, column tile): the r * tiles
   // workgroups of one (sequence, K-head) get ids 8 apart, so they land on one
@@ -922,9 +934,10 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   if (si.slot < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
-  const bool rec = wave < 4;                   // recurrence wave
-  const int w4 = wave & 3;                     // token-row block (and state row block)
-  const int i0 = 16 * w4 + 4 * lk;             // first of this lane's four token rows
+  const bool rec = wave < NRW;                 // recurrence wave
+  // token-row block (and first state row block): the wave's index within its role
+  const int w4 = NRW == 4 ? (wave & 3) : (rec ? wave : wave - NRW);
+  const int i0 = 16 * (w4 & 3) + 4 * lk;       // first of this lane's four token rows
   float* Sg = p.rec + ((size_t)si.slot * p.Hv + h) * D * D;
   const size_t cbase = si.len > 0 ? chunk_base_of(p, n) : 0;
   const int nchunks = (si.len + kL - 1) / kL;
@@ -943,7 +956,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
     float v[RBW][NCB][4];
 #pragma unroll
     for (int q = 0; q < RBW; ++q) {
-      const int rb = min(w4 + 4 * q, NRB - 1);
+      const int rb = min(w4 + NRW * q, NRB - 1);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -953,7 +966,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
     const unsigned keep_bits = si.init ? ~0u : 0u;
 #pragma unroll
     for (int q = 0; q < RBW; ++q)
-      if (w4 + 4 * q < NRB)
+      if (w4 + NRW * q < NRB)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -965,7 +978,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   if (rec)
 #pragma unroll
     for (int q = 0; q < RBW; ++q) {
-      const int rb = w4 + 4 * q;
+      const int rb = w4 + NRW * q;
       if (rb < NRB)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -987,9 +1000,12 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
   // (chunk index clamped), so the prefetch of chunk c+1 never introduces a
   // branch and its wait.
   const auto chunk_loop = [&](auto role) {
-    constexpr bool REC = decltype(role)::value;
+    constexpr int ROLE = decltype(role)::value;
+    constexpr bool REC = ROLE < 2;       // carries state row blocks
+    constexpr bool VP = ROLE == 0;       // forms V' in the first phase
     ChunkOps<NKS, RBW, NCB> ops;
     auto load_fa = [&](int c) {
+      if constexpr (ROLE == 1) return;   // no first-phase product
       const size_t mat = REC ? (cbase + c) * p.Hv + h : (cbase + c) * p.Hk + m;
       const __bf16* hi = REC ? p.s.w[0] : p.s.qh[0];
       const __bf16* lo = REC ? p.s.w[1] : p.s.qh[1];
@@ -1005,7 +1021,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       const __bf16* lo = REC ? p.s.kt[1] : p.s.pm[1];
 #pragma unroll
       for (int q = 0; q < (REC ? RBW : 1); ++q) {   // output waves need one P row block
-        const int rb = min(w4 + 4 * q, NRB - 1);
+        const int rb = min(w4 + NRW * q, NRB - 1);
         const size_t blk0 = REC ? (((cbase + c) * p.Hk + m) * NRB + rb) * 2
                                 : (((cbase + c) * p.Hv + h) * 4 + w4) * 2;
 #pragma unroll
@@ -1019,13 +1035,25 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
     auto load_misc = [&](int c) {
       const int nc = min(kL, si.len - c * kL);
       const size_t gh = (cbase + c) * p.Hv + h;
-      if constexpr (REC)
+      if constexpr (VP)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           ops.u[cb] = *reinterpret_cast<const f32x4*>(
               p.s.ut + (((gh * NRB + col0 / 16 + cb) * 4 + w4) * 64 + lane) * 4);
-      ops.gam = *reinterpret_cast<const f32x4*>(p.s.gam + gh * kL + i0);
+      if constexpr (ROLE != 1) ops.gam = *reinterpret_cast<const f32x4*>(p.s.gam + gh * kL + i0);
       ops.glast = p.s.gam[gh * kL + nc - 1];
+    };
+
+    // (state-only waves) chunk c-1's staged outputs to global memory
+    long long otok0 = 0;
+    int onc = 0;
+    auto flush_o = [&]() {
+      static_assert(!STAGE_O || 2 * kL <= 64 * (NRW - 4), "staging copy fits the waves");
+      const int idx = (wave - 4) * 64 + lane, i = idx >> 1, half = idx & 1;
+      if (i < onc)
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.obuf) +
+                                   ((size_t)(otok0 + i) * p.Hv + h) * D + col0 + 8 * half) =
+            *reinterpret_cast<const bf16x8*>(&sO[i * DVT + 8 * half]);
     };
 
     if (nchunks > 0) {  // same issue order as in the loop (see its waits)
@@ -1043,15 +1071,22 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       // chunk at once, so their loads are the oldest outstanding ones a
       // chunk later
       f32x4 u[NCB];
+      f32x4 gam = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (VP)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) u[cb] = ops.u[cb];
-      const f32x4 gam = ops.gam;
+        for (int cb = 0; cb < NCB; ++cb) u[cb] = ops.u[cb];
+      if constexpr (ROLE != 1) gam = ops.gam;
       const float glast = ops.glast;
       load_misc(cn);
+      if constexpr (STAGE_O && ROLE == 1) {
+        if (c > 0) flush_o();
+        otok0 = tok0;
+        onc = nc;
+      }
       // phase 1: V' = U - W S_c (recurrence waves) / Y = Q S_c (output waves)
       f32x4 O[NCB];
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int cb = 0; cb < (ROLE == 1 ? 0 : NCB); ++cb) {
         f32x4 r1;
         if constexpr (!REC && OB) {
           // output-only product, single pass (bf16 output path)
@@ -1060,7 +1095,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
           for (int ks = 0; ks < NKS; ++ks)
             r1 = mfma_bf16(ops.fa[ks][0], ld8(&sS[0][(16 * cb + li) * LS + 32 * ks + 8 * lk]), r1);
         } else {
-          Acc3 acc = acc3(REC ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+          Acc3 acc = acc3(VP ? u[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const int bo = (16 * cb + li) * LS + 32 * ks + 8 * lk;
@@ -1092,7 +1127,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
         const float egl = __expf(glast);
 #pragma unroll
         for (int q = 0; q < RBW; ++q) {
-          const int rb = w4 + 4 * q;
+          const int rb = w4 + NRW * q;
           if (rb < NRB)
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
@@ -1131,13 +1166,19 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
             }
             o = fold(ao);
           }
+          if constexpr (STAGE_O) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i0 + e;
-            const size_t at = ((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li;
-            if (i < nc) {
-              if constexpr (OB) reinterpret_cast<__bf16*>(p.obuf)[at] = static_cast<__bf16>(o[e]);
-              else p.obuf[at] = o[e];
+            for (int e = 0; e < 4; ++e)
+              sO[(i0 + e) * DVT + 16 * cb + li] = static_cast<__bf16>(o[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = i0 + e;
+              const size_t at = ((size_t)(tok0 + i) * p.Hv + h) * D + col0 + 16 * cb + li;
+              if (i < nc) {
+                if constexpr (OB) reinterpret_cast<__bf16*>(p.obuf)[at] = static_cast<__bf16>(o[e]);
+                else p.obuf[at] = o[e];
+              }
             }
           }
         }
@@ -1145,16 +1186,24 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
       load_fb(cn);
       __syncthreads();  // S_{c+1} is in LDS; every read of V' is done
     }
+    if constexpr (STAGE_O && ROLE == 1)
+      if (nchunks > 0) flush_o();   // the last chunk's outputs (after its closing barrier)
   };
-  if (rec)
-    chunk_loop(WaveRole<true>{});
-  else
-    chunk_loop(WaveRole<false>{});
+  if (!rec) {
+    chunk_loop(WaveRole<2>{});
+  } else if constexpr (NRW == 4) {
+    chunk_loop(WaveRole<0>{});
+  } else {
+    if (wave < 4)
+      chunk_loop(WaveRole<0>{});
+    else
+      chunk_loop(WaveRole<1>{});
+  }
 
   if (rec)
 #pragma unroll
     for (int q = 0; q < RBW; ++q) {
-      const int rb = w4 + 4 * q;
+      const int rb = w4 + NRW * q;
       if (rb < NRB)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -1172,7 +1221,7 @@ __global__ __launch_bounds__(kSNT) void prefill_state_kernel(PrefillParams p) {
     const int nch = DVT + (qk ? 2 * D : 0);
     const int vbase = 2 * p.Hk * D + h * D + col0;
     void* win = static_cast<char*>(p.conv) + (size_t)si.slot * K * p.C * io::bytes;
-    for (int e = tid; e < nch; e += kSNT) {
+    for (int e = tid; e < nch; e += NTH) {
       const int ch = e < DVT ? vbase + e
                    : e < DVT + D ? m * D + (e - DVT)
                                  : (p.Hk + m) * D + (e - DVT - D);
@@ -1289,10 +1338,11 @@ static void launch_state(const PrefillParams& p, hipStream_t st) {
   const long long units = (long long)p.N * p.Hk, per = (long long)p.r * (D / (16 * NCB));
   const long long groups = (units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * per));
+  constexpr int nth = state_threads<NCB>();
   if (p.o_bf16)
-    prefill_state_kernel<Act, D, K, NCB, true><<<grid, kSNT, 0, st>>>(p);
+    prefill_state_kernel<Act, D, K, NCB, true><<<grid, nth, 0, st>>>(p);
   else
-    prefill_state_kernel<Act, D, K, NCB, false><<<grid, kSNT, 0, st>>>(p);
+    prefill_state_kernel<Act, D, K, NCB, false><<<grid, nth, 0, st>>>(p);
 }
 
 template <typename Act, int D, int K>

@@ -215,15 +215,20 @@ def test_prefill_equals_decode_steps():
     np.testing.assert_array_equal(host(Pa.conv), host(Pb.conv))
 
 
-@pytest.mark.parametrize("case", ["packed", "t4096"])
+@pytest.mark.parametrize("case", ["packed", "narrow", "t4096"])
 def test_prefill_without_o_raw(case):
     """The call without o_raw, as a serving caller makes it (the pre-norm
     output then stays internal): y, states and conv windows against the
-    oracle, padding rows zero, untouched slots unchanged."""
+    oracle, padding rows zero, untouched slots unchanged.  "narrow" has few
+    enough sequences for 16-column state tiles, with partial last chunks."""
     if case == "packed":
         s = wl.RANK_LOCAL
         w, rec, conv, cu, d = _packed(700, s, [70, 1, 200, 64, 129], 8)
         slots, has_init = [5, 0, -1, 2, 7], [1, 1, 1, 0, 1]
+    elif case == "narrow":
+        s = wl.RANK_LOCAL
+        w, rec, conv, cu, d = _packed(701, s, [70, 5, 129], 8)
+        slots, has_init = [3, -1, 6], [1, 1, 0]
     else:
         work = wl.prefill_single(seed=0)
         s, d = work.shape, work.data
