@@ -914,10 +914,12 @@ __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(Pre
   __shared__ __attribute__((aligned(16))) __bf16 sS[2][DVT * LS];   // S_c, B operand
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][DVT * LR];   // V'
   __shared__ __attribute__((aligned(16))) __bf16 sD[2][DVT * LR];   // e^{gamma_L - gamma} V'
-  // bf16 outputs with eight recurrence waves: the output waves leave a
-  // chunk's O here and the state-only recurrence waves, idle in the next
-  // chunk's first phase, write it out with 16-byte stores
-  constexpr bool STAGE_O = OB && NRW == 8;
+  // bf16 outputs: the output waves leave a chunk's O here and, during the
+  // next chunk's first phase, where they wait on the recurrence, write it
+  // out with 16-byte stores (with eight recurrence waves the four that are
+  // idle in that phase do it instead)
+  constexpr bool STAGE_O = OB;
+  constexpr int FLUSH_ROLE = NRW == 8 ? 1 : 2;
   __shared__ __attribute__((aligned(16))) __bf16 sO[STAGE_O ? kL * DVT : 8];
 
   // Workgroup id -> (sequence, V-head, column tile): the r * tiles
@@ -1048,12 +1050,16 @@ __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(Pre
     long long otok0 = 0;
     int onc = 0;
     auto flush_o = [&]() {
-      static_assert(!STAGE_O || 2 * kL <= 64 * (NRW - 4), "staging copy fits the waves");
-      const int idx = (wave - 4) * 64 + lane, i = idx >> 1, half = idx & 1;
-      if (i < onc)
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.obuf) +
-                                   ((size_t)(otok0 + i) * p.Hv + h) * D + col0 + 8 * half) =
-            *reinterpret_cast<const bf16x8*>(&sO[i * DVT + 8 * half]);
+      constexpr int PR = DVT / 8;                 // 16-byte pieces per token row
+      const int first = (NRW == 8 ? wave - 4 : wave - NRW) * 64 + lane;
+#pragma unroll
+      for (int q = first; q < kL * PR; q += 256) {   // four flushing waves
+        const int i = q / PR, part = q % PR;
+        if (i < onc)
+          *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.obuf) +
+                                     ((size_t)(otok0 + i) * p.Hv + h) * D + col0 + 8 * part) =
+              *reinterpret_cast<const bf16x8*>(&sO[i * DVT + 8 * part]);
+      }
     };
 
     if (nchunks > 0) {  // same issue order as in the loop (see its waits)
@@ -1078,7 +1084,7 @@ __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(Pre
       if constexpr (ROLE != 1) gam = ops.gam;
       const float glast = ops.glast;
       load_misc(cn);
-      if constexpr (STAGE_O && ROLE == 1) {
+      if constexpr (STAGE_O && ROLE == FLUSH_ROLE) {
         if (c > 0) flush_o();
         otok0 = tok0;
         onc = nc;
@@ -1186,7 +1192,7 @@ __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(Pre
       load_fb(cn);
       __syncthreads();  // S_{c+1} is in LDS; every read of V' is done
     }
-    if constexpr (STAGE_O && ROLE == 1)
+    if constexpr (STAGE_O && ROLE == FLUSH_ROLE)
       if (nchunks > 0) flush_o();   // the last chunk's outputs (after its closing barrier)
   };
   if (!rec) {
