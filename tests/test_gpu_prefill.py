@@ -215,7 +215,7 @@ def test_prefill_equals_decode_steps():
     np.testing.assert_array_equal(host(Pa.conv), host(Pb.conv))
 
 
-@pytest.mark.parametrize("case", ["packed", "narrow", "t4096"])
+@pytest.mark.parametrize("case", ["packed", "narrow", "t4096", "varlen"])
 def test_prefill_without_o_raw(case):
     """The call without o_raw, as a serving caller makes it (the pre-norm
     output then stays internal): y, states and conv windows against the
@@ -230,23 +230,26 @@ def test_prefill_without_o_raw(case):
         w, rec, conv, cu, d = _packed(701, s, [70, 5, 129], 8)
         slots, has_init = [3, -1, 6], [1, 1, 0]
     else:
-        work = wl.prefill_single(seed=0)
+        work = wl.prefill_single(seed=0) if case == "t4096" else wl.prefill_varlen(seed=0)
         s, d = work.shape, work.data
         w, rec, conv, cu = d["weights"], d["rec"], d["conv"], d["cu_seqlens"]
         slots, has_init = d["slot_idx"], d["has_init"]
+    heads = [0, 1, 17, 30] if case == "varlen" else None   # sampled at full head count
     print(f"[prefill without o_raw] {case} T={int(cu[-1])}", flush=True)
     L = Layer(s, w)
     P = Pool(s, rec, conv)
     y, _ = prefill(L, P, cu, slots, d["x"], d["z"], d["a"], d["b"], has_init=has_init,
                    want_o=False)
     torch.cuda.synchronize()
-    yo, _, S, W = _oracle_prefill(L, rec, conv, cu, slots, d, np.asarray(has_init, np.uint8))
+    yo, _, S, W = _oracle_prefill(L, rec, conv, cu, slots, d, np.asarray(has_init, np.uint8),
+                                  heads=heads)
+    hs = np.arange(s.num_v_heads) if heads is None else np.asarray(heads)
     yh = host(y)
     live = np.asarray([sl for sl in slots if sl >= 0])
     tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
                           if slots[n] >= 0]).astype(np.int64)
-    assert_close("y", maxrel_heads(yh[tok], yo[tok]), y_tol(s))
-    assert_close("state", maxrel_states(host(P.rec)[live], S[live]), TOL_F32)
+    assert_close("y", maxrel_heads(yh[tok][:, hs], yo[tok][:, hs]), y_tol(s))
+    assert_close("state", maxrel_states(host(P.rec)[live][:, hs], S[live][:, hs]), TOL_F32)
     np.testing.assert_array_equal(host(P.conv)[live], W[live])
     pad = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
                           if slots[n] < 0] + [np.zeros(0, np.int64)]).astype(np.int64)
