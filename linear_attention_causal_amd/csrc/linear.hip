@@ -14,8 +14,8 @@
 //     waves split K and request every weight and input fragment of their K
 //     range before the first MFMA, and add their partial tiles through LDS.
 //   tile (M > 32): a dense product.  A workgroup owns a BM x BN output tile
-//     (the largest of 128 x 128 (eight waves), 128 x 64, 64 x 64 (four) that
-//     still gives 128 workgroups); x and w tiles of 32 k-columns are staged through three
+//     (128 x 128 with eight waves or 128 x 64 with four, the larger that
+//     still gives 128 workgroups, else 64 x 32 with two); x and w tiles of 32 k-columns are staged through three
 //     LDS buffers in MFMA fragment order, so each wave reads its operands
 //     with linear 16-byte LDS reads, and the input rows are fetched once
 //     per BN columns instead of once per 16.  Global loads run eight
@@ -302,7 +302,9 @@ LinearPlan linear_plan(int M, const LinearOut* outs, int count) {
   const long long rows128 = (M + 127) / 128;
   if (cols128 * rows128 >= 128) return {LinearPlan::kTile, 128, 128};
   if (cols64 * rows128 >= 128) return {LinearPlan::kTile, 128, 64};
-  return {LinearPlan::kTile, 64, 64};
+  // otherwise 64 x 32 tiles of two waves: twice the workgroups of 64 x 64
+  // tiles, so the product spreads over twice the CUs
+  return {LinearPlan::kTile, 64, 32};
 }
 
 hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* outs, int count,
@@ -325,7 +327,7 @@ hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* 
     return launch(linear_tile_kernel<128, 128, 8, 8>, p, outs, 128, 128, 512, stream);
   if (plan.rows == 128)
     return launch(linear_tile_kernel<128, 64, 8, 4>, p, outs, 64, 128, 256, stream);
-  return launch(linear_tile_kernel<64, 64, 8, 4>, p, outs, 64, 64, 256, stream);
+  return launch(linear_tile_kernel<64, 32, 8, 2>, p, outs, 32, 64, 128, stream);
 }
 
 }  // namespace gdn
