@@ -880,10 +880,10 @@ template <int R> struct WaveRole { static constexpr int value = R; };
 
 // Operands of one chunk held in registers by one wave of the state kernel;
 // the next chunk's are fetched into the same registers right after their
-// last use.  The same registers serve both wave roles:
-//   waves 0-3 (the recurrence)  fa = -W rows, fb = k_hat^T rows of the owned
-//                               state row blocks, u = U tiles
-//   waves 4-7 (the outputs)     fa = q_hat rows, fb[0] = P rows
+// last use.  The same registers serve every wave role:
+//   recurrence waves   fa = -W rows (those that form V'), fb = k_hat^T rows
+//                      of the owned state row blocks, u = U tiles
+//   output waves       fa = q_hat rows, fb[0] = P rows
 template <int NKS, int RBW, int NCB>
 struct ChunkOps {
   bf16x8 fa[NKS][2];
@@ -896,10 +896,10 @@ struct ChunkOps {
 // One workgroup per (sequence, V-head, 16 NCB state columns), one pass over
 // the sequence's chunks (chunk recurrence of the WY form: V' = U - W S,
 // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) V', O = e^gamma Q S + P V').
-// Waves 0-3 carry the recurrence; waves 4-7 compute the chunk's outputs from
-// the same S and V' tiles in LDS, beside it, so the serial chain per chunk
-// is two contractions and two barriers.  Every operand fetch is one
-// contiguous 1 KB fragment block per wave.
+// The first NRW waves carry the recurrence; the last four compute the
+// chunk's outputs from the same S and V' tiles in LDS, beside it, so the
+// serial chain per chunk is two contractions and two barriers.  Every
+// operand fetch is one contiguous 1 KB fragment block per wave.
 template <typename Act, int D, int K, int NCB, bool OB>
 __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(PrefillParams p) {
   using io = act_io<Act>;
