@@ -38,21 +38,27 @@ def _oracle_prefill(L, rec, conv, cu, slots, d, has_init=None, heads=None):
     return y, o, S, W
 
 
-def _check_prefill(s, w, rec, conv, cu, slots, d, has_init=None, heads=None, tag=""):
-    print(f"[prefill] {tag} T={int(cu[-1])} N={len(cu) - 1}", flush=True)
+def _check_prefill(s, w, rec, conv, cu, slots, d, has_init=None, heads=None, tag="",
+                   want_o=True):
+    """Parity of one packed prefill; want_o=False makes the call without o_raw
+    (a bf16 layer then takes its bf16 output path) and checks y and the states."""
+    print(f"[prefill] {tag} T={int(cu[-1])} N={len(cu) - 1} o_raw={want_o}", flush=True)
     L = Layer(s, w)
     P = Pool(s, rec, conv)
-    y, o = prefill(L, P, cu, slots, d["x"], d["z"], d["a"], d["b"], has_init=has_init)
+    y, o = prefill(L, P, cu, slots, d["x"], d["z"], d["a"], d["b"], has_init=has_init,
+                   want_o=want_o)
     torch.cuda.synchronize()
     yo, oo, S, W = _oracle_prefill(L, rec, conv, cu, slots, d, has_init, heads)
     hs = np.arange(s.num_v_heads) if heads is None else np.asarray(heads)
-    yh, oh = host(y), host(o)
+    yh = host(y)
+    oh = host(o) if want_o else np.zeros_like(yh)
     live = np.asarray([sl for sl in slots if sl >= 0])
     tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(slots))
                           if slots[n] >= 0] + [np.zeros(0, np.int64)]).astype(np.int64)
     if tok.size:
         assert_close("y", maxrel_heads(yh[tok][:, hs], yo[tok][:, hs]), y_tol(s))
-        assert_close("o_raw", maxrel_heads(oh[tok][:, hs], oo[tok][:, hs]), TOL_F32)
+        if want_o:
+            assert_close("o_raw", maxrel_heads(oh[tok][:, hs], oo[tok][:, hs]), TOL_F32)
     rec_gpu, conv_gpu = host(P.rec), host(P.conv)
     if live.size:
         assert_close("state", maxrel_states(rec_gpu[live][:, hs], S[live][:, hs]), TOL_F32)
@@ -82,7 +88,8 @@ def test_prefill_ragged_single(T):
     _check_prefill(s, w, rec, conv, cu, np.array([1], np.int32), d, tag=f"f32 d32 T={T}")
 
 
-def test_prefill_packed_mixed_bf16():
+@pytest.mark.parametrize("want_o", [True, False])
+def test_prefill_packed_mixed_bf16(want_o):
     """Packed sequences with a zero-length one, a fresh start (has_init = 0),
     a padding sequence (slot -1) and partial last chunks."""
     s = wl.Shape(4, 8, 64, 64, 4, "bf16")
@@ -90,7 +97,8 @@ def test_prefill_packed_mixed_bf16():
     slots = np.array([4, 0, 7, -1, 2, 5], np.int32)
     init = np.array([1, 1, 0, 1, 0, 1], np.uint8)
     w, rec, conv, cu, d = _packed(200, s, lens, 9)
-    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="packed bf16 d64")
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="packed bf16 d64",
+                   want_o=want_o)
 
 
 @pytest.mark.parametrize("K", [2, 3])
@@ -100,7 +108,8 @@ def test_prefill_conv_widths(K):
     _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"K={K}")
 
 
-def test_prefill_many_sequences_device_prefix():
+@pytest.mark.parametrize("want_o", [True, False])
+def test_prefill_many_sequences_device_prefix(want_o):
     """70 packed sequences (more than the launch carries inline, so the chunk
     prefix is formed on the device), with empty ones, padding and fresh starts."""
     s = wl.Shape(2, 4, 32, 32, 4, "bf16")
@@ -112,11 +121,13 @@ def test_prefill_many_sequences_device_prefix():
     slots[[5, 33]] = -1
     init = (rng.random(N) < 0.7).astype(np.uint8)
     w, rec, conv, cu, d = _packed(601, s, list(lens), P)
-    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="70 sequences")
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="70 sequences",
+                   want_o=want_o)
 
 
+@pytest.mark.parametrize("want_o", [True, False])
 @pytest.mark.parametrize("N", [3, 70])
-def test_prefill_all_sequences_empty(N):
+def test_prefill_all_sequences_empty(N, want_o):
     """No tokens at all (T = 0, no scratch): each slot keeps its state and
     window, or is reset to zeros for a fresh start; padding untouched."""
     s = wl.Shape(2, 4, 32, 32, 4, "bf16")
@@ -126,16 +137,19 @@ def test_prefill_all_sequences_empty(N):
     slots[1] = -1
     init = (rng.random(N) < 0.5).astype(np.uint8)
     w, rec, conv, cu, d = _packed(701 + N, s, [0] * N, P)
-    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag=f"{N} empty sequences")
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag=f"{N} empty sequences",
+                   want_o=want_o)
 
 
+@pytest.mark.parametrize("want_o", [True, False])
 @pytest.mark.parametrize("Hk,Hv", [(1, 8), (2, 6), (4, 4)])
-def test_prefill_gqa_ratios(Hk, Hv):
+def test_prefill_gqa_ratios(Hk, Hv, want_o):
     """8, 3 and 1 V-heads per K-head (the prep kernel forms the gates in
     groups of up to four V-heads)."""
     s = wl.Shape(Hk, Hv, 32, 32, 4, "bf16")
     w, rec, conv, cu, d = _packed(500 + Hv, s, [97, 40], 3)
-    _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"Hk={Hk} Hv={Hv}")
+    _check_prefill(s, w, rec, conv, cu, np.array([2, 0], np.int32), d, tag=f"Hk={Hk} Hv={Hv}",
+                   want_o=want_o)
 
 
 def test_prefill_slow_decay_long_carry():
