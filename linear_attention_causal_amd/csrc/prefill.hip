@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(Pre
       ops.glast = p.s.gam[gh * kL + nc - 1];
     };
 
-    // (state-only waves) chunk c-1's staged outputs to global memory
+    // chunk c-1's staged outputs to global memory, written by the FLUSH_ROLE waves
     long long otok0 = 0;
     int onc = 0;
     auto flush_o = [&]() {
