@@ -135,10 +135,11 @@ def bench_decode(args):
     R = args.replicas
     layers = [DecodeLayer(gdn, geom, work.data, act) for _ in range(R)]
     y = torch.empty(B, geom.num_v_heads, geom.head_v_dim, device="cuda", dtype=act)
+    ws = gdn.decode_workspace(geom, B)
 
     def step(i, stream):
         L = layers[i % R]
-        gdn.gdn_decode_step(geom, L.w, L.pool, L.slot, L.x, L.z, L.a, L.b, y, stream=stream)
+        gdn.gdn_decode_step(geom, L.w, L.pool, L.slot, L.x, L.z, L.a, L.b, y, ws, stream=stream)
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -403,6 +404,7 @@ def bench_block(B, shape, P, replicas):
     aa = torch.empty(B, Hv, device="cuda", dtype=bf)
     y = torch.empty(B, vd, device="cuda", dtype=bf)
     out = torch.empty(B, H, device="cuda", dtype=bf)
+    ws = gdn.decode_workspace(geom, B)
 
     def in_proj(r, st):
         R = reps[r]
@@ -410,7 +412,7 @@ def bench_block(B, shape, P, replicas):
                                 (R["p"]["a"], aa)], stream=st)
 
     def core(r, st):
-        gdn.gdn_decode_step(geom, lw, reps[r]["pool"], slot, qkv, z, aa, bb, y, stream=st)
+        gdn.gdn_decode_step(geom, lw, reps[r]["pool"], slot, qkv, z, aa, bb, y, ws, stream=st)
 
     def out_proj(r, st):
         gdn.gdn_linear(y, [(reps[r]["p"]["out"], out)], stream=st)
@@ -502,10 +504,11 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
     # device-resident slot index: the captured step reads it, a retire event
     # rewrites it in place
     slot_d = _t(live, torch.int32)
+    ws = gdn.decode_workspace(geom, B)
 
     def layer_pass(st):
         for L in Ls:
-            gdn.gdn_decode_step(geom, L["w"], L["pool"], slot_d, x, z, a, b, y, stream=st)
+            gdn.gdn_decode_step(geom, L["w"], L["pool"], slot_d, x, z, a, b, y, ws, stream=st)
 
     graph = None
 

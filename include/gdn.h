@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 enum {
   GDN_OK = 0,
@@ -68,7 +68,7 @@ enum {
   GDN_E_SLOT = -5,        /* host-visible slot out of range or duplicated */
   GDN_E_OVERLAP = -6,     /* compaction source and destination sets meet */
   GDN_E_SEQLENS = -7,     /* cu_seqlens not 0-based / non-decreasing */
-  GDN_E_SCRATCH = -8,     /* scratch buffer missing or too small */
+  GDN_E_SCRATCH = -8,     /* scratch or workspace missing or too small */
   GDN_E_HIP = -9,         /* the HIP runtime reported an error at launch */
   GDN_E_ALIGN = -10       /* a device array is not 16-byte aligned (scratch:
                              256-byte) */
@@ -159,23 +159,34 @@ int gdn_decode_batch(const gdn_geometry* geom, const gdn_layer_weights* w,
                      const void* z, const void* a, const void* b, void* y,
                      float* o_raw, void* stream);
 
+/* Bytes of the workspace gdn_decode_step needs for up to B rows: a
+ * workspace of this size serves every call with B or fewer rows.  It holds
+ * one call's arrival counters (B * Hk * (2 dk / 64) words, rounded up to
+ * 256 bytes) and scales with the rows, not with the pool. */
+int gdn_decode_workspace_bytes(const gdn_geometry* geom, int32_t B, size_t* bytes);
+
 /* Fused decode step: gdn_conv_update followed by gdn_decode_batch for the
  * same rows, in one launch and without the f32 conv-output round trip (the
- * batched decode chain of pegainfer issue #1001, Splits, with the conv and
- * the state update of one layer in a single kernel).  Arguments as in those
- * two calls; qkv_in [B][C] act.  Results equal the two-call sequence.
- * One workgroup runs per (row, V-head); the Hv/Hk workgroups that share a
- * K-head's q/k conv window agree on which of them writes it back through
- * arrival counters the library keeps per (slot number, K-head, 64 q/k
- * channels), zero between calls.  Any Hv/Hk is taken while num_slots * Hk *
- * (2 dk / 64) <= 65536; past that a per-K-head kernel runs, for Hv/Hk in
- * {1, 2, 4} (otherwise GDN_E_UNSUPPORTED).  Two calls that overlap in time on
- * one GPU must not name the same slot number, even in different pools. */
+ * batched decode chain of pegainfer issue #1001, Splits, "Batched eager TP
+ * decode", with the conv and the state update of one layer in a single
+ * kernel).  Arguments as in those two calls; qkv_in [B][C] act.  Results
+ * equal the two-call sequence.
+ * workspace: caller-owned device memory of at least
+ * gdn_decode_workspace_bytes(geom, B) bytes, 256-byte aligned, ZERO-FILLED
+ * before its first use; every call leaves it zero-filled again, so one
+ * allocation serves any number of calls, on any pool, one at a time.  Calls
+ * that may run at the same time (other streams) need separate workspaces;
+ * they may name the same slot numbers in different pools.  One workgroup
+ * runs per (row, V-head); the Hv/Hk workgroups that share a K-head's q/k
+ * conv window count their reads of it in the workspace, and the last reader
+ * writes the shifted window back.  Nothing in the library keeps state
+ * between calls. */
 int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
                     const gdn_state_pool* pool, const int32_t* slot_idx,
                     const int32_t* slot_idx_host, int32_t B, const void* qkv_in,
                     const void* z, const void* a, const void* b, void* y,
-                    float* o_raw, void* stream);
+                    float* o_raw, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* ------------------------------------------------------------- prefill */
 

@@ -17,7 +17,8 @@ from . import _abi
 from ._abi import GDN_BF16, GDN_F32, GdnError
 
 __all__ = ["Geometry", "LayerWeights", "StatePool", "GdnError", "gdn_slot_bytes",
-           "gdn_prefill_scratch_bytes", "gdn_conv_update", "gdn_decode_batch",
+           "gdn_prefill_scratch_bytes", "gdn_decode_workspace_bytes", "decode_workspace",
+           "gdn_conv_update", "gdn_decode_batch",
            "gdn_decode_step", "gdn_prefill_chunked", "gdn_state_compact", "gdn_linear",
            "library"]
 
@@ -131,6 +132,21 @@ def gdn_prefill_scratch_bytes(geom: Geometry, total_tokens: int, num_seqs: int) 
     return n.value
 
 
+def gdn_decode_workspace_bytes(geom: Geometry, B: int) -> int:
+    lib = _abi.load()
+    n = ctypes.c_size_t()
+    g = geom.c()
+    _abi.check(lib.gdn_decode_workspace_bytes(ctypes.byref(g), int(B), ctypes.byref(n)))
+    return n.value
+
+
+def decode_workspace(geom: Geometry, B: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace for gdn_decode_step calls of up to B
+    rows (torch allocates it; the library keeps it zero between calls)."""
+    return torch.zeros(max(gdn_decode_workspace_bytes(geom, B), 256), dtype=torch.uint8,
+                       device=device)
+
+
 def gdn_conv_update(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx: torch.Tensor,
                     qkv_in: torch.Tensor, qkv_out: torch.Tensor, slot_idx_host=None,
                     stream=None) -> None:
@@ -167,13 +183,17 @@ def gdn_decode_batch(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx:
 
 def gdn_decode_step(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx: torch.Tensor,
                     qkv_in: torch.Tensor, z: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
-                    y: torch.Tensor, o_raw: torch.Tensor | None = None, slot_idx_host=None,
-                    stream=None) -> None:
+                    y: torch.Tensor, workspace: torch.Tensor, o_raw: torch.Tensor | None = None,
+                    slot_idx_host=None, stream=None) -> None:
+    """workspace: a uint8 device tensor from decode_workspace (zero-filled
+    before first use, left zero-filled by every call)."""
     lib = _abi.load()
     B = slot_idx.numel()
     Hv, dv = geom.num_v_heads, geom.head_v_dim
     act = geom.act_dtype
     _, host = _host_i32(slot_idx_host, B, "slot_idx_host")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
     g = geom.c()
     _abi.check(lib.gdn_decode_step(
         ctypes.byref(g), ctypes.byref(w.c), ctypes.byref(pool.c),
@@ -181,6 +201,7 @@ def gdn_decode_step(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx: 
         _ptr(qkv_in, act, B * geom.channels, "qkv_in"),
         _ptr(z, act, B * Hv * dv, "z"), _ptr(a, act, B * Hv, "a"), _ptr(b, act, B * Hv, "b"),
         _ptr(y, act, B * Hv * dv, "y"), _ptr(o_raw, torch.float32, B * Hv * dv, "o_raw"),
+        _ptr(workspace, name="workspace"), workspace.numel() if workspace is not None else 0,
         _stream(stream)))
 
 

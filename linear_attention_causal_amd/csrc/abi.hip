@@ -184,17 +184,23 @@ int gdn_decode_batch(const gdn_geometry* geom, const gdn_layer_weights* w,
                     "gdn_decode_batch launch");
 }
 
+int gdn_decode_workspace_bytes(const gdn_geometry* geom, int32_t B, size_t* bytes) {
+  GDN_TRY(check_geometry(geom));
+  if (!bytes) return fail(GDN_E_NULL, "output pointer is NULL");
+  if (B < 0) return fail(GDN_E_SHAPE, "B = %d is negative", B);
+  if ((long long)B * geom->num_v_heads > (1LL << 30)) return fail(GDN_E_SHAPE, "B too large");
+  *bytes = gdn::decode_workspace_bytes(*geom, B);
+  return ok();
+}
+
 int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
                     const gdn_state_pool* pool, const int32_t* slot_idx,
                     const int32_t* slot_idx_host, int32_t B, const void* qkv_in, const void* z,
-                    const void* a, const void* b, void* y, float* o_raw, void* stream) {
+                    const void* a, const void* b, void* y, float* o_raw, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   GDN_TRY(check_geometry(geom));
   GDN_TRY(check_weights(w));
   GDN_TRY(check_pool(pool, true, true));
-  if (!gdn::decode_step_supported(*geom, pool->num_slots))
-    return fail(GDN_E_UNSUPPORTED,
-                "fused decode step: Hv/Hk must be 1, 2 or 4 for a pool of %d slots",
-                pool->num_slots);
   if (B < 0) return fail(GDN_E_SHAPE, "B = %d is negative", B);
   if ((long long)B * geom->num_v_heads > (1LL << 30)) return fail(GDN_E_SHAPE, "B too large");
   if (B == 0) return ok();
@@ -202,9 +208,16 @@ int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
     return fail(GDN_E_NULL, "a device array is NULL");
   if (!aligned16(qkv_in) || !aligned16(z) || !aligned16(y) || (o_raw && !aligned16(o_raw)))
     return fail(GDN_E_ALIGN, "qkv_in, z, y, o_raw must be 16-byte aligned");
+  const size_t need = gdn::decode_workspace_bytes(*geom, B);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_E_SCRATCH, "workspace needs %zu bytes for %d rows, got %zu", need, B,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
   GDN_TRY(check_slots_host(slot_idx_host, B, pool->num_slots));
   return hip_status(gdn::launch_decode_step(*geom, *w, *pool, slot_idx, B, qkv_in, z, a, b, y,
-                                            o_raw, static_cast<hipStream_t>(stream)),
+                                            o_raw, workspace,
+                                            static_cast<hipStream_t>(stream)),
                     "gdn_decode_step launch");
 }
 

@@ -255,248 +255,41 @@ struct StepParams {
   const float* A_log;
   const float* dt_bias;
   const float* norm_w;
+  unsigned int* arrivals;   // workspace [B][Hk][2D/64]: readers of a q/k window
   int B, Hk, Hv, C, num_slots;
   int r;                // Hv / Hk
   int per_xcd;          // (row, V-head) units per XCD lane of the grid
   float l2eps, rmseps, scale;
 };
 
-// One workgroup per (row, K-head): the conv of the K-head's q/k channels and
-// of the v channels of its R V-heads (so every conv-window channel has one
-// owner), then R independent state steps on groups of HT = 2D threads.
-// Order of work inside a group, chosen so that HBM is busy throughout:
-//   1. the small conv inputs are requested first, then the state tile in NQ
-//      column chunks;
-//   2. conv + SiLU, l2 norms and gates run while the tile streams in;
-//   3. chunk 0 is reduced (kappa = S^T k, rho = S^T q), updated and stored
-//      while the later chunks' loads are still arriving; then chunk 1, ...;
-//   4. gated RMSNorm over all chunks' outputs.
-constexpr int kDecodeChunks = 1;   // column chunks of the state tile (NQ)
-constexpr int kStepThreadsPerDim = 2;  // threads per V-head = this * D
-
-template <typename Act, int D, int R, int K>
-__global__ __launch_bounds__(kStepThreadsPerDim * D * R) void decode_step_kernel(StepParams p) {
-  using io = act_io<Act>;
-  constexpr int NQ = kDecodeChunks;
-  constexpr int HT = kStepThreadsPerDim * D;   // threads per V-head
-  constexpr int NT = HT * R;
-  constexpr int CW = D / NQ;         // columns per chunk
-  constexpr int CGH = CW / 4;        // four-column groups per chunk
-  constexpr int RG = HT / CGH;       // row groups
-  constexpr int RPT = D / RG;        // rows per thread per chunk
-  constexpr int HW = HT / 64;        // waves per V-head
-  constexpr int NCH = (2 + R) * D;   // channels this workgroup convolves
-  constexpr int CPT = (NCH + NT - 1) / NT;
-  static_assert(HT % 64 == 0 && CGH <= 64 && 64 % CGH == 0 && RPT >= 1, "layout");
-
-  __shared__ float s_x[NCH];         // conv + SiLU output: q, k, v_0 .. v_{R-1}
-  __shared__ f32x4 s_red[R][NQ][HW][2][CGH];
-
-  const int tid = threadIdx.x;
-  const int grp = tid / HT, gt = tid - grp * HT;   // V-head within the K-head, thread in group
-  const int lane = tid & 63, gwave = gt >> 6;
-  const int cgh = gt % CGH, rg = gt / CGH;
-  const int row = blockIdx.x / p.Hk;
-  const int m = blockIdx.x - row * p.Hk;
-  const int h = m * R + grp;
-  const size_t out_off = ((size_t)row * p.Hv + h) * D;
-  const int slot = p.slot_idx[row];
-  if (slot < 0 || slot >= p.num_slots) {  // padding row: zeros, no state access
-    for (int j = gt; j < D; j += HT) {
-      io::store(p.y, out_off + j, 0.f);
-      if (p.o_raw) p.o_raw[out_off + j] = 0.f;
-    }
-    return;
-  }
-
-  // 1. conv inputs (window columns 1..K-1, the token, the weights), then the tile
-  void* win = static_cast<char*>(p.conv) + (size_t)slot * K * p.C * io::bytes;
-  float col[CPT][K], wt[CPT][K];
-  int chs[CPT];
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) {
-    const int e = tid + q * NT;
-    const int ee = e < NCH ? e : 0;
-    const int part = ee / D, j = ee - part * D;
-    chs[q] = part == 0 ? m * D + j
-           : part == 1 ? (p.Hk + m) * D + j
-                       : 2 * p.Hk * D + (m * R + part - 2) * D + j;
-#pragma unroll
-    for (int k = 1; k < K; ++k) col[q][k - 1] = io::load(win, (size_t)k * p.C + chs[q]);
-    col[q][K - 1] = io::load(p.x, (size_t)row * p.C + chs[q]);
-#pragma unroll
-    for (int k = 0; k < K; ++k) wt[q][k] = io::load(p.weight, (size_t)chs[q] * K + k);
-  }
-  const float a_in = io::load(p.a, (size_t)row * p.Hv + h);
-  const float b_in = io::load(p.b, (size_t)row * p.Hv + h);
-  // read here: below the window stores the compiler could not move these
-  // loads up (they might alias), and they would cost a second round trip
-  const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
-  // compiler-only fence: the small loads above are issued before the tile's,
-  // so the conv can start when they arrive (a wait counts loads in issue
-  // order); without it the conv loads get sunk below the tile's loads
-  asm volatile("" ::: "memory");
-  float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
-  f32x4 s[NQ][RPT];
-#pragma unroll
-  for (int hf = 0; hf < NQ; ++hf)
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      s[hf][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-          S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
-
-  // 2. conv + SiLU; shifted window written back (raw inputs: lossless).
-  // The sums are formed for every slot, outside the guard: used only inside
-  // it, the conv loads would be sunk below the tile's loads and, counted in
-  // order, wait for the whole tile.
-  float acc[CPT];
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) {
-    acc[q] = 0.f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) acc[q] = fmaf(wt[q][k], col[q][k], acc[q]);
-  }
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) {
-    const int e = tid + q * NT;
-    if (e < NCH) {
-      s_x[e] = silu(acc[q]);
-#pragma unroll
-      for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chs[q], col[q][k]);
-    }
-  }
-  float g, beta;
-  gates(A_log, dt_bias, a_in, b_in, g, beta);
-  const float eg = expf(g);
-  __syncthreads();
-
-  const float* sq = s_x;
-  const float* sk = s_x + D;
-  const float* sv = s_x + (2 + grp) * D;
-  float sqq = 0.f, skk = 0.f, sqk = 0.f;
-  for (int j = lane; j < D; j += 64) {
-    const float qv = sq[j], kv = sk[j];
-    sqq = fmaf(qv, qv, sqq);
-    skk = fmaf(kv, kv, skk);
-    sqk = fmaf(qv, kv, sqk);
-  }
-  sqq = wave_sum(sqq);
-  skk = wave_sum(skk);
-  sqk = wave_sum(sqk);
-  const float rq = p.scale / sqrtf(sqq + p.l2eps);
-  const float rk = 1.0f / sqrtf(skk + p.l2eps);
-  const float kq = sqk * rq * rk;
-  float kr[RPT], qr[RPT];   // k_hat, q_hat at this thread's rows
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    kr[i] = sk[rg + RG * i] * rk;
-    qr[i] = sq[rg + RG * i] * rq;
-  }
-
-  // 3. per column chunk: reduce, update, store
-  f32x4 o[NQ];
-#pragma unroll
-  for (int hf = 0; hf < NQ; ++hf) {
-    f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      kap += s[hf][i] * kr[i];
-      rho += s[hf][i] * qr[i];
-    }
-#pragma unroll
-    for (int off = CGH; off < 64; off <<= 1) {
-      kap.x += __shfl_xor(kap.x, off, 64); kap.y += __shfl_xor(kap.y, off, 64);
-      kap.z += __shfl_xor(kap.z, off, 64); kap.w += __shfl_xor(kap.w, off, 64);
-      rho.x += __shfl_xor(rho.x, off, 64); rho.y += __shfl_xor(rho.y, off, 64);
-      rho.z += __shfl_xor(rho.z, off, 64); rho.w += __shfl_xor(rho.w, off, 64);
-    }
-    if (lane < CGH) {
-      s_red[grp][hf][gwave][0][cgh] = kap;
-      s_red[grp][hf][gwave][1][cgh] = rho;
-    }
-    __syncthreads();
-    kap = s_red[grp][hf][0][0][cgh];
-    rho = s_red[grp][hf][0][1][cgh];
-#pragma unroll
-    for (int w = 1; w < HW; ++w) {
-      kap += s_red[grp][hf][w][0][cgh];
-      rho += s_red[grp][hf][w][1][cgh];
-    }
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[hf * CW + 4 * cgh]);
-    const f32x4 u = beta * (v - eg * kap);
-    o[hf] = eg * rho + u * kq;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      f32x4 ns;
-      ns.x = fmaf(eg, s[hf][i].x, kr[i] * u.x);
-      ns.y = fmaf(eg, s[hf][i].y, kr[i] * u.y);
-      ns.z = fmaf(eg, s[hf][i].z, kr[i] * u.z);
-      ns.w = fmaf(eg, s[hf][i].w, kr[i] * u.w);
-      __builtin_nontemporal_store(
-          ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
-    }
-  }
-
-  // 4. gated RMSNorm over the D outputs of this head (first wave of the group;
-  // every row group holds all columns, so the xor-reduction over the CGH
-  // lanes of a row group yields the full sum)
-  if (gwave == 0) {
-    float ss = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < NQ; ++hf)
-      ss += o[hf].x * o[hf].x + o[hf].y * o[hf].y + o[hf].z * o[hf].z + o[hf].w * o[hf].w;
-#pragma unroll
-    for (int off = 1; off < CGH; off <<= 1) ss += __shfl_xor(ss, off, 64);
-    const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
-    if (lane < CGH) {
-#pragma unroll
-      for (int hf = 0; hf < NQ; ++hf) {
-        const int c0 = hf * CW + 4 * cgh;
-        const f32x4 nw = *reinterpret_cast<const f32x4*>(p.norm_w + c0);
-        const f32x4 zz = io::load4(p.z, out_off + c0);
-        f32x4 yv;
-        yv.x = nw.x * o[hf].x * inv * silu(zz.x);
-        yv.y = nw.y * o[hf].y * inv * silu(zz.y);
-        yv.z = nw.z * o[hf].z * inv * silu(zz.z);
-        yv.w = nw.w * o[hf].w * inv * silu(zz.w);
-        io::store4(p.y, out_off + c0, yv);
-        if (p.o_raw) *reinterpret_cast<f32x4*>(p.o_raw + out_off + c0) = o[hf];
-      }
-    }
-  }
-}
-
-// Arrival counters of decode_head_kernel: one per (slot, K-head, wave of q/k
-// channels).  Zero between calls.
-constexpr int kArrivalCounters = 1 << 16;
-__device__ unsigned int g_arrivals[kArrivalCounters];
-
-// One workgroup of 2D threads per (row, V-head): twice the workgroups of the
-// per-K-head kernel above, so each CU moves half as many state bytes (the
-// per-CU load path, not HBM, sets a small batch's time).  The r = Hv/Hk
-// workgroups of one (row, K-head) each convolve the K-head's q/k channels
-// from the old conv window; the shifted q/k window may be written only after
-// all r have read it.  Each wave holds 64 q/k channels and, once its loads of
-// them have returned, adds one to the (slot, K-head, wave) counter; the
-// arrival that finds r-1 (mod r) earlier arrivals is the last reader, writes
-// those channels' shifted window and takes r back off the counter.  Nobody
-// waits for anybody.  The v channels of V-head h have one reader, their own
-// workgroup, which writes them back at once.  Block x runs unit
-// (x % 8) * per_xcd + x / 8, which keeps the r units of a (row, K-head) on
-// one XCD (blocks are dealt to the eight XCDs in turn).
-template <typename Act, int D, int K, int NQ>
+// One workgroup of 2D threads per (row, V-head): the whole state tile of one
+// head is read once and written once by the same workgroup, which also
+// holds every output of the head for the gated RMSNorm.
+//
+// q/k conv window.  The r = Hv/Hk workgroups of one (row, K-head) each
+// convolve the K-head's q/k channels from the old window, and the shifted
+// window may be written back only after all r have read it.  Each wave
+// holds 64 q/k channels and, once its loads of them have returned, adds one
+// to the counter of (row, K-head, wave) in the caller's workspace; the
+// arrival that finds r-1 (mod r) earlier arrivals is the last reader,
+// writes those channels' shifted window and takes r back off the counter,
+// so the counters are zero between calls and nobody waits for anybody.  A
+// v channel has one reader, its V-head's workgroup, which writes it back
+// itself.  Block x runs unit (x % 8) * per_xcd + x / 8, which keeps the r
+// units of a (row, K-head) on one XCD (blocks are dealt to the eight XCDs
+// in turn) and so their window reads in one L2.
+template <typename Act, int D, int K>
 __global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
   using io = act_io<Act>;
-  constexpr int NT = 2 * D;          // threads of the V-head
-  constexpr int CW = D / NQ;         // columns per chunk
-  constexpr int CGH = CW / 4;        // four-column groups per chunk
+  constexpr int NT = 2 * D;          // threads
+  constexpr int CGH = D / 4;         // four-column groups
   constexpr int RG = NT / CGH;       // row groups
-  constexpr int RPT = D / RG;        // rows per thread per chunk
+  constexpr int RPT = D / RG;        // rows per thread
   constexpr int HW = NT / 64;        // waves (each holds 64 of the 2D q/k channels)
   static_assert(NT % 64 == 0 && CGH <= 64 && 64 % CGH == 0 && RPT >= 1, "layout");
 
   __shared__ float s_x[3 * D];       // conv + SiLU output: q, k, v_h
-  __shared__ f32x4 s_red[NQ][HW][2][CGH];
+  __shared__ f32x4 s_red[HW][2][CGH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -542,27 +335,20 @@ __global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
   const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
   // the epilogue's z and norm weight too (every thread, its four columns),
   // so the end of the kernel waits on no load
-  typename io::raw4_t rz[NQ];
-  f32x4 nw[NQ];
-#pragma unroll
-  for (int hf = 0; hf < NQ; ++hf) {
-    rz[hf] = io::load4_raw(p.z, out_off + hf * CW + 4 * cgh);
-    nw[hf] = *reinterpret_cast<const f32x4*>(p.norm_w + hf * CW + 4 * cgh);
-  }
+  const typename io::raw4_t rz = io::load4_raw(p.z, out_off + 4 * cgh);
+  const f32x4 nw = *reinterpret_cast<const f32x4*>(p.norm_w + 4 * cgh);
   __builtin_amdgcn_sched_barrier(0);
   float* S = p.rec + ((size_t)slot * p.Hv + h) * D * D;
   // issued in the order the reduction consumes them (the scheduler otherwise
   // reverses it and the first product waits for the whole tile); nothing
   // moves across the barriers
-  f32x4 s[NQ][RPT];
+  f32x4 s[RPT];
 #pragma unroll
-  for (int hf = 0; hf < NQ; ++hf)
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      s[hf][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-          S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int i = 0; i < RPT; ++i) {
+    s[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(S + (size_t)(rg + RG * i) * D + 4 * cgh));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float cq[K], wq[K], cv[K], wv[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -572,9 +358,7 @@ __global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
     wv[k] = io::from_raw(rwv[k]);
   }
   const float a_in = io::from_raw(ra), b_in = io::from_raw(rb);
-  f32x4 zz[NQ];
-#pragma unroll
-  for (int hf = 0; hf < NQ; ++hf) zz[hf] = io::from_raw4(rz[hf]);
+  const f32x4 zz = io::from_raw4(rz);
 
   // 2. conv + SiLU
   float accq = 0.f, accv = 0.f;
@@ -585,22 +369,15 @@ __global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
   }
   s_x[tid] = silu(accq);
   if (tid < D) s_x[2 * D + tid] = silu(accv);
-  // The v window is written back by every thread (those past D repeat
-  // channel D-1 with its own values): stores under a branch between the
-  // tile's loads and their use would make the reduction wait for all of them
-  // at once instead of load by load.
-#pragma unroll
-  for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chv, cv[k]);
   // arrival (lane 0 of each wave; one atomic per wave); the increment takes
   // accq as an operand (through an empty asm), so it issues only after this
   // wave's q/k window loads have returned
-  const size_t ctr = ((size_t)slot * p.Hk + m) * HW + wave;
+  unsigned int* ctr = p.arrivals + ((size_t)row * p.Hk + m) * HW + wave;
   unsigned int arrived = 0;
   unsigned int one = 1;
   asm volatile("" : "+v"(one) : "v"(accq));
   if (lane == 0 && p.r > 1)
-    arrived = __hip_atomic_fetch_add(&g_arrivals[ctr], one, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+    arrived = __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float g, beta;
   gates(A_log, dt_bias, a_in, b_in, g, beta);
   const float eg = expf(g);
@@ -629,77 +406,73 @@ __global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
     qr[i] = sq[rg + RG * i] * rq;
   }
 
-  // 3. per column chunk (a chunk's columns need only its own loads): reduce
-  // (kappa = S^T k, rho = S^T q), update, store
-  f32x4 o[NQ];
+  // 3. reduce (kappa = S^T k, rho = S^T q), update, store
+  f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int hf = 0; hf < NQ; ++hf) {
-    f32x4 kap = {0.f, 0.f, 0.f, 0.f}, rho = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RPT; ++i) {
+    kap += s[i] * kr[i];
+    rho += s[i] * qr[i];
+  }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      kap += s[hf][i] * kr[i];
-      rho += s[hf][i] * qr[i];
-    }
+  for (int off = CGH; off < 64; off <<= 1) {
+    kap.x += __shfl_xor(kap.x, off, 64); kap.y += __shfl_xor(kap.y, off, 64);
+    kap.z += __shfl_xor(kap.z, off, 64); kap.w += __shfl_xor(kap.w, off, 64);
+    rho.x += __shfl_xor(rho.x, off, 64); rho.y += __shfl_xor(rho.y, off, 64);
+    rho.z += __shfl_xor(rho.z, off, 64); rho.w += __shfl_xor(rho.w, off, 64);
+  }
+  if (lane < CGH) {
+    s_red[wave][0][cgh] = kap;
+    s_red[wave][1][cgh] = rho;
+  }
+  __syncthreads();
+  kap = s_red[0][0][cgh];
+  rho = s_red[0][1][cgh];
 #pragma unroll
-    for (int off = CGH; off < 64; off <<= 1) {
-      kap.x += __shfl_xor(kap.x, off, 64); kap.y += __shfl_xor(kap.y, off, 64);
-      kap.z += __shfl_xor(kap.z, off, 64); kap.w += __shfl_xor(kap.w, off, 64);
-      rho.x += __shfl_xor(rho.x, off, 64); rho.y += __shfl_xor(rho.y, off, 64);
-      rho.z += __shfl_xor(rho.z, off, 64); rho.w += __shfl_xor(rho.w, off, 64);
-    }
-    if (lane < CGH) {
-      s_red[hf][wave][0][cgh] = kap;
-      s_red[hf][wave][1][cgh] = rho;
-    }
-    __syncthreads();
-    kap = s_red[hf][0][0][cgh];
-    rho = s_red[hf][0][1][cgh];
+  for (int w = 1; w < HW; ++w) {
+    kap += s_red[w][0][cgh];
+    rho += s_red[w][1][cgh];
+  }
+  const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[4 * cgh]);
+  const f32x4 u = beta * (v - eg * kap);
+  const f32x4 o = eg * rho + u * kq;
 #pragma unroll
-    for (int w = 1; w < HW; ++w) {
-      kap += s_red[hf][w][0][cgh];
-      rho += s_red[hf][w][1][cgh];
-    }
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&sv[hf * CW + 4 * cgh]);
-    const f32x4 u = beta * (v - eg * kap);
-    o[hf] = eg * rho + u * kq;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      f32x4 ns;
-      ns.x = fmaf(eg, s[hf][i].x, kr[i] * u.x);
-      ns.y = fmaf(eg, s[hf][i].y, kr[i] * u.y);
-      ns.z = fmaf(eg, s[hf][i].z, kr[i] * u.z);
-      ns.w = fmaf(eg, s[hf][i].w, kr[i] * u.w);
-      __builtin_nontemporal_store(
-          ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + hf * CW + 4 * cgh));
-    }
+  for (int i = 0; i < RPT; ++i) {
+    f32x4 ns;
+    ns.x = fmaf(eg, s[i].x, kr[i] * u.x);
+    ns.y = fmaf(eg, s[i].y, kr[i] * u.y);
+    ns.z = fmaf(eg, s[i].z, kr[i] * u.z);
+    ns.w = fmaf(eg, s[i].w, kr[i] * u.w);
+    __builtin_nontemporal_store(
+        ns, reinterpret_cast<f32x4*>(S + (size_t)(rg + RG * i) * D + 4 * cgh));
   }
 
   // 4. gated RMSNorm over the D outputs (first wave; each row group holds all
   // columns, so the xor-reduction over its CGH lanes gives the full sum)
   if (wave == 0) {
-    float ss = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < NQ; ++hf)
-      ss += o[hf].x * o[hf].x + o[hf].y * o[hf].y + o[hf].z * o[hf].z + o[hf].w * o[hf].w;
+    float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
 #pragma unroll
     for (int off = 1; off < CGH; off <<= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = 1.0f / sqrtf(ss / D + p.rmseps);
     if (lane < CGH) {
-#pragma unroll
-      for (int hf = 0; hf < NQ; ++hf) {
-        const int c0 = hf * CW + 4 * cgh;
-        f32x4 yv;
-        yv.x = nw[hf].x * o[hf].x * inv * silu(zz[hf].x);
-        yv.y = nw[hf].y * o[hf].y * inv * silu(zz[hf].y);
-        yv.z = nw[hf].z * o[hf].z * inv * silu(zz[hf].z);
-        yv.w = nw[hf].w * o[hf].w * inv * silu(zz[hf].w);
-        io::store4(p.y, out_off + c0, yv);
-        if (p.o_raw) *reinterpret_cast<f32x4*>(p.o_raw + out_off + c0) = o[hf];
-      }
+      f32x4 yv;
+      yv.x = nw.x * o.x * inv * silu(zz.x);
+      yv.y = nw.y * o.y * inv * silu(zz.y);
+      yv.z = nw.z * o.z * inv * silu(zz.z);
+      yv.w = nw.w * o.w * inv * silu(zz.w);
+      io::store4(p.y, out_off + 4 * cgh, yv);
+      if (p.o_raw) *reinterpret_cast<f32x4*>(p.o_raw + out_off + 4 * cgh) = o;
     }
   }
 
-  // 5. the last reader of this wave's q/k channels writes their shifted window
+  // 5. the shifted v window, by the thread that owns each channel.  Threads
+  // past D loaded channel D-1 as well; storing it from them too would race
+  // with their own loads in other waves.  Here every wave is past the first
+  // barrier, so all window loads of this workgroup have returned.
+  if (tid < D) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chv, cv[k]);
+  }
+  // 6. the last reader of this wave's q/k channels writes their shifted window
   bool last = true;
   if (p.r > 1) {
     const unsigned int before = __builtin_amdgcn_readfirstlane(arrived);
@@ -709,21 +482,26 @@ __global__ __launch_bounds__(2 * D) void decode_head_kernel(StepParams p) {
 #pragma unroll
     for (int k = 0; k < K; ++k) io::store(win, (size_t)k * p.C + chq, cq[k]);
     if (p.r > 1 && lane == 0)
-      __hip_atomic_fetch_add(&g_arrivals[ctr], 0u - (unsigned int)p.r, __ATOMIC_RELAXED,
+      __hip_atomic_fetch_add(ctr, 0u - (unsigned int)p.r, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-constexpr int kHeadChunks = 1;   // column chunks of the state tile (NQ)
+// Workspace of gdn_decode_step: the arrival counters [B][Hk][2D/64] u32
+// (row-keyed, so its size follows the rows of a call and a workspace for B
+// rows serves every smaller call).
+size_t decode_workspace_bytes(const gdn_geometry& g, long long B) {
+  const long long words = B * g.num_k_heads * (2LL * g.head_k_dim / 64);
+  return ((size_t)words * 4 + 255) & ~size_t(255);
+}
 
 template <typename Act, int D>
 static hipError_t head_k(const StepParams& p, int K, hipStream_t st) {
   dim3 grid(8 * p.per_xcd);
-  constexpr int NQ = kHeadChunks;
   switch (K) {
-    case 2: decode_head_kernel<Act, D, 2, NQ><<<grid, 2 * D, 0, st>>>(p); break;
-    case 3: decode_head_kernel<Act, D, 3, NQ><<<grid, 2 * D, 0, st>>>(p); break;
-    case 4: decode_head_kernel<Act, D, 4, NQ><<<grid, 2 * D, 0, st>>>(p); break;
+    case 2: decode_head_kernel<Act, D, 2><<<grid, 2 * D, 0, st>>>(p); break;
+    case 3: decode_head_kernel<Act, D, 3><<<grid, 2 * D, 0, st>>>(p); break;
+    case 4: decode_head_kernel<Act, D, 4><<<grid, 2 * D, 0, st>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -739,56 +517,10 @@ static hipError_t head_d(const StepParams& p, int D, int K, hipStream_t st) {
   }
 }
 
-// The per-V-head kernel runs when its counters cover the pool's slots (or
-// when no K-head is shared); otherwise the per-K-head kernel.
-static bool use_head_kernel(const gdn_geometry& g, int num_slots) {
-  const int r = g.num_v_heads / g.num_k_heads;
-  const long long waves = 2LL * g.head_k_dim / 64;
-  return r == 1 || (long long)num_slots * g.num_k_heads * waves <= kArrivalCounters;
-}
-
-template <typename Act, int D, int R>
-static hipError_t step_k(const StepParams& p, int K, hipStream_t st) {
-  dim3 grid(p.B * p.Hk);
-  constexpr int NT = kStepThreadsPerDim * D * R;
-  switch (K) {
-    case 2: decode_step_kernel<Act, D, R, 2><<<grid, NT, 0, st>>>(p); break;
-    case 3: decode_step_kernel<Act, D, R, 3><<<grid, NT, 0, st>>>(p); break;
-    case 4: decode_step_kernel<Act, D, R, 4><<<grid, NT, 0, st>>>(p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <typename Act, int D>
-static hipError_t step_r(const StepParams& p, int R, int K, hipStream_t st) {
-  switch (R) {
-    case 1: return step_k<Act, D, 1>(p, K, st);
-    case 2: return step_k<Act, D, 2>(p, K, st);
-    case 4: return step_k<Act, D, 4>(p, K, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <typename Act>
-static hipError_t step_d(const StepParams& p, int D, int R, int K, hipStream_t st) {
-  switch (D) {
-    case 32: return step_r<Act, 32>(p, R, K, st);
-    case 64: return step_r<Act, 64>(p, R, K, st);
-    case 128: return step_r<Act, 128>(p, R, K, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-bool decode_step_supported(const gdn_geometry& g, int num_slots) {
-  const int r = g.num_v_heads / g.num_k_heads;
-  return use_head_kernel(g, num_slots) || r == 2 || r == 4;
-}
-
 hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
                               const gdn_state_pool& pool, const int32_t* slot_idx, int B,
                               const void* qkv_in, const void* z, const void* a, const void* b,
-                              void* y, float* o_raw, hipStream_t stream) {
+                              void* y, float* o_raw, void* workspace, hipStream_t stream) {
   StepParams p;
   p.x = qkv_in;
   p.weight = w.conv_weight;
@@ -803,6 +535,7 @@ hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
   p.A_log = w.A_log;
   p.dt_bias = w.dt_bias;
   p.norm_w = w.norm_weight;
+  p.arrivals = static_cast<unsigned int*>(workspace);
   p.B = B;
   p.Hk = g.num_k_heads;
   p.Hv = g.num_v_heads;
@@ -811,18 +544,12 @@ hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
   p.l2eps = g.l2norm_eps;
   p.rmseps = g.rmsnorm_eps;
   p.scale = g.scale > 0.f ? g.scale : 1.0f / sqrtf((float)g.head_k_dim);
-  const int R = g.num_v_heads / g.num_k_heads;
-  p.r = R;
-  if (use_head_kernel(g, pool.num_slots)) {
-    const int units = B * p.Hv;
-    const int per = (units + 7) / 8;
-    p.per_xcd = (per + R - 1) / R * R;   // a (row, K-head) never straddles two XCDs
-    if (g.act_dtype == GDN_BF16) return head_d<__bf16>(p, g.head_k_dim, g.conv_kernel, stream);
-    return head_d<float>(p, g.head_k_dim, g.conv_kernel, stream);
-  }
-  p.per_xcd = 0;
-  if (g.act_dtype == GDN_BF16) return step_d<__bf16>(p, g.head_k_dim, R, g.conv_kernel, stream);
-  return step_d<float>(p, g.head_k_dim, R, g.conv_kernel, stream);
+  p.r = g.num_v_heads / g.num_k_heads;
+  const long long units = (long long)B * p.Hv;
+  const long long per = (units + 7) / 8;
+  p.per_xcd = (int)((per + p.r - 1) / p.r * p.r);   // a (row, K-head) never straddles two XCDs
+  if (g.act_dtype == GDN_BF16) return head_d<__bf16>(p, g.head_k_dim, g.conv_kernel, stream);
+  return head_d<float>(p, g.head_k_dim, g.conv_kernel, stream);
 }
 
 // ------------------------------------------------------------- launchers

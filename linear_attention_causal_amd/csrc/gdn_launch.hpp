@@ -18,12 +18,14 @@ hipError_t launch_decode(const gdn_geometry& g, const gdn_layer_weights& w,
                          const float* qkv, const void* z, const void* a,
                          const void* b, void* y, float* o_raw, hipStream_t stream);
 
-bool decode_step_supported(const gdn_geometry& g, int num_slots);
+// Workspace bytes of the fused step for up to B rows (any call with B' <= B
+// fits).
+size_t decode_workspace_bytes(const gdn_geometry& g, long long B);
 
 hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
                               const gdn_state_pool& pool, const int32_t* slot_idx, int B,
                               const void* qkv_in, const void* z, const void* a, const void* b,
-                              void* y, float* o_raw, hipStream_t stream);
+                              void* y, float* o_raw, void* workspace, hipStream_t stream);
 
 // Token-indexed scratch layout of the chunkwise prefill (see prefill.hip).
 size_t prefill_scratch_bytes(const gdn_geometry& g, long long total_tokens,

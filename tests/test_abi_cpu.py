@@ -34,11 +34,11 @@ def host_i32(vals):
 
 def test_exports_every_declared_function():
     names = _abi.header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(_abi.PROTOTYPES) == set(names)
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
 
 
 def test_status_strings():
@@ -123,20 +123,46 @@ def test_decode_batch_checks():
     assert _decode(slots_host=h) == _abi.GDN_E_SLOT
 
 
-def test_decode_step_head_ratio_checks():
-    """gdn_decode_step takes any Hv/Hk while its per-(slot, K-head) arrival
-    counters cover the pool; past that it falls back to the per-K-head kernel,
-    which exists for Hv/Hk in {1, 2, 4}.  B = 0 returns before any launch."""
-    def step(g, P, B=0):
+def _ws_bytes(g, B):
+    n = ctypes.c_size_t()
+    assert lib.gdn_decode_workspace_bytes(ctypes.byref(g), B, ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_decode_workspace_sizes():
+    """The workspace scales with the rows, not the pool, and a workspace sized
+    for B rows serves every smaller call (the size never decreases with B)."""
+    for g in (geom(), geom(Hk=16, Hv=32), geom(Hk=2, Hv=4, d=32), geom(Hk=4, Hv=16, d=64)):
+        sizes = [_ws_bytes(g, B) for B in range(0, 300)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+        assert all(x % 256 == 0 for x in sizes)
+    # q/k counters alone past the split rows: B * Hk * (2 d / 64) words
+    g = geom(Hk=16, Hv=32)
+    big = _ws_bytes(g, 4096) - _ws_bytes(g, 2048)
+    assert big == 2048 * 16 * 4 * 4
+    n = ctypes.c_size_t()
+    assert lib.gdn_decode_workspace_bytes(ctypes.byref(g), -1, ctypes.byref(n)) == \
+        _abi.GDN_E_SHAPE
+    assert lib.gdn_decode_workspace_bytes(ctypes.byref(g), 4, None) == _abi.GDN_E_NULL
+
+
+def test_decode_step_checks():
+    """gdn_decode_step: any Hv/Hk and any pool size; the workspace is checked
+    (missing, too small, misaligned) before anything is enqueued.  Every call
+    below carries a planted error, so none reaches a launch."""
+    def step(g, P=64, B=4, ws=V(0x400000), nbytes=1 << 30, z=DEV):
         w, p = weights(), pool(P)
         return lib.gdn_decode_step(ctypes.byref(g), ctypes.byref(w), ctypes.byref(p), DEV, None,
-                                   B, DEV, DEV, DEV, DEV, DEV, None, None)
-    g3 = geom(Hk=2, Hv=6, d=32)          # one wave of q/k channels per K-head
-    assert step(g3, P=32768) == 0        # 2 * 32768 counters: covered
-    assert step(g3, P=32769) == _abi.GDN_E_UNSUPPORTED
-    assert step(geom(Hk=2, Hv=4, d=32), P=1 << 20) == 0    # falls back
-    assert step(geom(Hk=16, Hv=16), P=1 << 20) == 0        # r = 1 needs no counter
-    assert step(geom(Hk=2, Hv=4, d=32), P=64, B=-1) == _abi.GDN_E_SHAPE
+                                   B, DEV, z, DEV, DEV, DEV, None, ws, nbytes, None)
+    g = geom()
+    assert step(g, B=0, ws=None, nbytes=0) == 0                  # empty: no-op
+    assert step(g, B=-1) == _abi.GDN_E_SHAPE
+    assert step(g, ws=None) == _abi.GDN_E_SCRATCH
+    assert step(g, nbytes=_ws_bytes(g, 4) - 1) == _abi.GDN_E_SCRATCH
+    assert step(g, ws=V(0x400010)) == _abi.GDN_E_ALIGN
+    assert step(g, z=None) == _abi.GDN_E_NULL
+    assert step(geom(Hk=2, Hv=6, d=32), P=1 << 20, ws=None) == _abi.GDN_E_SCRATCH
+    assert b"workspace" in lib.gdn_last_error()
 
 
 def _prefill(cu, slots_host=None, scratch=DEV, nbytes=1 << 40, N=None):

@@ -1,16 +1,14 @@
 """GPU state compaction (gdn_state_compact): a bit-exact copy of whole slots
-across every layer, nothing else touched; and a decode schedule with retire /
-compact / admit whose sampled rows still match the oracle's per-sequence
-results."""
+across every layer, nothing else touched; and decode schedules with retire /
+compact / admit whose live rows all match the oracle's per-sequence results,
+up to the full-head serving shape."""
 import numpy as np
 import pytest
 import torch
 
 import linear_attention_causal_amd as gdn
-import oracle
 import workloads as wl
-from gpu_helpers import (TOL_F32, Layer, Pool, assert_close, decode_step, dev, host,
-                         maxrel_heads, maxrel_states, y_tol)
+from gpu_helpers import Layer, Pool, ServingRows, decode_step, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -35,10 +33,11 @@ def test_compaction_is_bitwise_copy(shape, L):
 
 
 def test_decode_schedule_with_retire_and_compaction():
-    """B=48 rows of a 64-slot pool, 2 layers, 24 steps; after steps 8 and 16 a
-    seeded half of the rows retire, survivors are compacted by hole filling
-    and new rows are admitted with zero state.  Sampled surviving rows are
-    compared with the oracle running each row's tokens as one sequence."""
+    """B=48 rows of a 64-slot pool, 2 layers, 24 steps of the two-call decode
+    (gdn_conv_update + gdn_decode_batch); after steps 8 and 16 a seeded half
+    of the rows retire, survivors are compacted by hole filling and new rows
+    are admitted with zero state.  Every live row at the end is compared with
+    the oracle running its tokens as one sequence."""
     s = wl.Shape(4, 8, 64, 64, 4, "bf16")
     rng = np.random.default_rng(11)
     P, B0, steps, layers = 64, 48, 24, 2
@@ -46,55 +45,62 @@ def test_decode_schedule_with_retire_and_compaction():
     init = [wl.state_pool(rng, s, P) for _ in range(layers)]
     Ls = [Layer(s, w) for w in ws]
     Ps = [Pool(s, *init[l]) for l in range(layers)]
-    slots0 = rng.choice(P, B0, replace=False).astype(np.int32)
-    # logical rows: initial slot (None = admitted fresh), tokens seen, last-layer y
-    rows = [dict(start=int(sl), toks=[]) for sl in slots0]
-    active = list(range(B0))
-    slot_of = {i: int(slots0[i]) for i in active}
+    rows = ServingRows(rng.choice(P, B0, replace=False).astype(np.int32))
     for t in range(steps):
         if t in (8, 16):
-            live = np.array([slot_of[i] for i in active], np.int32)
-            keep, new_slots, src, dst = wl.retire_plan(rng, live, P)
+            src, dst, free = rows.retire(rng, P)
             if src.size:
                 gdn.gdn_state_compact(Ls[0].geom, [p.pool for p in Ps], src, dst,
                                       dev(src, torch.int32), dev(dst, torch.int32))
-            survivors = [i for i, k in zip(active, keep) if k]
-            for i, ns in zip(survivors, new_slots):
-                slot_of[i] = int(ns)
-            n_new = len(active) - len(survivors)
-            free = list(range(len(survivors), len(survivors) + n_new))
             for p in Ps:   # admitted rows start from zero state
                 p.rec[free] = 0
                 p.conv[free] = 0
-            for f in free:
-                rows.append(dict(start=None, toks=[]))
-                slot_of[len(rows) - 1] = f
-            active = survivors + list(range(len(rows) - n_new, len(rows)))
-        inp = wl.token_inputs(rng, s, len(active))
-        sl = np.array([slot_of[i] for i in active], np.int32)
+        inp = wl.token_inputs(rng, s, len(rows.active))
+        sl = rows.live_slots()
         for l in range(layers):
             y, _ = decode_step(Ls[l], Ps[l], sl, inp["x"], inp["z"], inp["a"], inp["b"],
                                want_o=False)
-        yh = host(y)
-        for j, i in enumerate(active):
-            rows[i]["toks"].append({k: inp[k][j] for k in inp} | {"y": yh[j]})
-    sample = active[:: max(1, len(active) // 6)]
-    for i in sample:
-        r = rows[i]
-        tok = {k: np.stack([t[k] for t in r["toks"]]) for k in ("x", "z", "a", "b")}
-        T = len(r["toks"])
+        rows.record(inp, host(y))
+    rows.check(Ls, Ps, init, s, tag="two-call schedule")
+
+
+def test_serving_schedule_full_heads():
+    """The full-head serving shape: Hk=16, Hv=32, d=128, B=256 rows of a
+    320-slot pool, two layers run by the fused step with a device-resident
+    slot index and no host copy (as a replayed graph runs it), nine steps
+    with a retire event after steps 3 and 6: a seeded half of the rows
+    retire, survivors are compacted into the prefix by hole filling
+    (gdn_state_compact over both layers), new rows are admitted behind them
+    with zeroed state, and the device slot index is rewritten in place.
+    Every live row at the end (all 256) is checked against the oracle: both
+    layers' states and conv windows and the last layer's y for every token."""
+    s = wl.FULL_HEADS
+    rng = np.random.default_rng(13)
+    P, B, steps, layers = 320, 256, 9, 2
+    ws = [wl.layer_weights(rng, s) for _ in range(layers)]
+    init = [wl.state_pool(rng, s, P) for _ in range(layers)]
+    print(f"[schedule] full heads B={B} P={P} layers={layers} steps={steps}", flush=True)
+    Ls = [Layer(s, w) for w in ws]
+    Ps = [Pool(s, *init[l]) for l in range(layers)]
+    rows = ServingRows(rng.choice(P, B, replace=False).astype(np.int32))
+    slot_d = dev(rows.live_slots(), torch.int32)
+    wsp = gdn.decode_workspace(Ls[0].geom, B)
+    bf = torch.bfloat16
+    y = torch.empty(B, s.num_v_heads, s.head_v_dim, device="cuda", dtype=bf)
+    for t in range(steps):
+        if t in (3, 6):
+            src, dst, free = rows.retire(rng, P)
+            gdn.gdn_state_compact(Ls[0].geom, [p.pool for p in Ps], src, dst,
+                                  dev(src, torch.int32), dev(dst, torch.int32))
+            for p in Ps:
+                p.rec[free] = 0
+                p.conv[free] = 0
+            slot_d.copy_(dev(rows.live_slots(), torch.int32))
+            print(f"  step {t}: {src.size} slots moved, {len(free)} admitted", flush=True)
+        inp = wl.token_inputs(rng, s, B)
+        x, z, a, b = (dev(inp[k], bf) for k in ("x", "z", "a", "b"))
         for l in range(layers):
-            if r["start"] is None:
-                S0 = np.zeros((1, s.num_v_heads, s.head_k_dim, s.head_v_dim))
-                W0 = np.zeros((1, s.conv_kernel, s.channels))
-            else:
-                S0 = init[l][0][r["start"]][None].astype(np.float64)
-                W0 = init[l][1][r["start"]][None].astype(np.float64)
-            yo, _, Sn, Wn = oracle.sequences(Ls[l].og, Ls[l].ow, [0, T], tok["x"], tok["z"],
-                                             tok["a"], tok["b"], S0, W0)
-            assert_close(f"row {i} layer {l} state",
-                         maxrel_states(host(Ps[l].rec)[slot_of[i]], Sn[0]), TOL_F32)
-            np.testing.assert_array_equal(host(Ps[l].conv)[slot_of[i]], Wn[0])
-            if l == layers - 1:
-                ygpu = np.stack([t["y"] for t in r["toks"]])
-                assert_close(f"row {i} y", maxrel_heads(ygpu, yo), y_tol(s))
+            gdn.gdn_decode_step(Ls[l].geom, Ls[l].w, Ps[l].pool, slot_d, x, z, a, b, y, wsp)
+        rows.record(inp, host(y))
+    rows.check(Ls, Ps, init, s, tag="full-head schedule")
+    assert not wsp.any()

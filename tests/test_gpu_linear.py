@@ -100,6 +100,7 @@ def _block_gpu(L, P, proj_d, slots, hidden, s, H):
     gdn.gdn_linear(h, [(proj_d["qkv"], qkv), (proj_d["z"], z), (proj_d["b"], b),
                        (proj_d["a"], a)])
     gdn.gdn_decode_step(L.geom, L.w, P.pool, sl, qkv, z, a, b, y,
+                        gdn.decode_workspace(L.geom, B),
                         slot_idx_host=np.asarray(slots, np.int32))
     gdn.gdn_linear(y.view(B, vd), [(proj_d["out"], out)])
     torch.cuda.synchronize()

@@ -200,15 +200,28 @@ def test_prefill_rank_local_t4096():
                    d["slot_idx"], d, has_init=d["has_init"], tag=work.name)
 
 
-def test_prefill_varlen8_full_heads_sampled():
+def test_prefill_varlen8_full_heads():
     """Eight packed sequences of U(128, 8192) tokens at Hk=16, Hv=32, d=128,
-    per-sequence nonzero initial states; four V-heads (two sibling pairs)
-    checked against the oracle, conv windows of all channels checked."""
+    per-sequence nonzero initial states, with o_raw: every V-head's y, o_raw
+    and final state, every conv window, against the oracle."""
     work = wl.prefill_varlen(seed=0)
     d = work.data
     _check_prefill(work.shape, d["weights"], d["rec"], d["conv"], d["cu_seqlens"],
-                   d["slot_idx"], d, has_init=d["has_init"], heads=[0, 1, 17, 30],
-                   tag=work.name)
+                   d["slot_idx"], d, has_init=d["has_init"], tag=work.name)
+
+
+@pytest.mark.parametrize("lens,P", [([70, 1, 200, 64, 129], 8), ([300, 17, 64, 5, 130, 90, 1], 9)])
+def test_prefill_32_column_state_tiles_with_o_raw(lens, P):
+    """d=128 with o_raw at batch sizes whose state workgroups take 32 of the
+    128 state columns (5 or 7 sequences x 16 V-heads: the widest tile that
+    still gives about one workgroup per CU), including partial and one-token
+    chunks and a fresh start."""
+    s = wl.RANK_LOCAL
+    w, rec, conv, cu, d = _packed(800 + len(lens), s, lens, P)
+    slots = np.random.default_rng(len(lens)).choice(P, len(lens), replace=False).astype(np.int32)
+    init = np.ones(len(lens), np.uint8)
+    init[1] = 0
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag=f"32-column tiles {lens}")
 
 
 def test_prefill_equals_decode_steps():
@@ -248,7 +261,7 @@ def test_prefill_without_o_raw(case):
         s, d = work.shape, work.data
         w, rec, conv, cu = d["weights"], d["rec"], d["conv"], d["cu_seqlens"]
         slots, has_init = d["slot_idx"], d["has_init"]
-    heads = [0, 1, 17, 30] if case == "varlen" else None   # sampled at full head count
+    heads = None
     print(f"[prefill without o_raw] {case} T={int(cu[-1])}", flush=True)
     L = Layer(s, w)
     P = Pool(s, rec, conv)
