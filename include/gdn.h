@@ -188,6 +188,25 @@ int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
                     float* o_raw, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* gdn_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same step as gdn_decode_step, with its workspace taken
+ * from a device array the library holds, GDN_NOALLOC_WORKSPACE_BYTES per
+ * GPU (one copy on each GPU it runs on, held until the process ends; set up
+ * on the first call on a device, with a clear enqueued on `stream`).  A call
+ * whose rows need more workspace than that (gdn_decode_workspace_bytes) is
+ * rejected with GDN_E_SCRATCH before anything is enqueued; at Hk = 16 and
+ * dk = 128 that is past 4096 rows.  Every call on one GPU shares the array,
+ * which each call leaves zero-filled: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must not be made.  Allocates
+ * nothing. */
+#define GDN_NOALLOC_WORKSPACE_BYTES ((size_t)1 << 20)
+int gdn_decode_step_noalloc(const gdn_geometry* geom, const gdn_layer_weights* w,
+                            const gdn_state_pool* pool, const int32_t* slot_idx,
+                            const int32_t* slot_idx_host, int32_t B,
+                            const void* qkv_in, const void* z, const void* a,
+                            const void* b, void* y, float* o_raw, void* stream);
+
 /* ------------------------------------------------------------- prefill */
 
 /* Chunkwise prefill of N packed sequences (pegainfer PR #1003, PR body,

@@ -19,7 +19,7 @@ from ._abi import GDN_BF16, GDN_F32, GdnError
 __all__ = ["Geometry", "LayerWeights", "StatePool", "GdnError", "gdn_slot_bytes",
            "gdn_prefill_scratch_bytes", "gdn_decode_workspace_bytes", "decode_workspace",
            "gdn_conv_update", "gdn_decode_batch",
-           "gdn_decode_step", "gdn_prefill_chunked", "gdn_state_compact", "gdn_linear",
+           "gdn_decode_step", "gdn_decode_step_noalloc", "gdn_prefill_chunked", "gdn_state_compact", "gdn_linear",
            "library"]
 
 
@@ -202,6 +202,28 @@ def gdn_decode_step(geom: Geometry, w: LayerWeights, pool: StatePool, slot_idx: 
         _ptr(z, act, B * Hv * dv, "z"), _ptr(a, act, B * Hv, "a"), _ptr(b, act, B * Hv, "b"),
         _ptr(y, act, B * Hv * dv, "y"), _ptr(o_raw, torch.float32, B * Hv * dv, "o_raw"),
         _ptr(workspace, name="workspace"), workspace.numel() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def gdn_decode_step_noalloc(geom: Geometry, w: LayerWeights, pool: StatePool,
+                            slot_idx: torch.Tensor, qkv_in: torch.Tensor, z: torch.Tensor,
+                            a: torch.Tensor, b: torch.Tensor, y: torch.Tensor,
+                            o_raw: torch.Tensor | None = None, slot_idx_host=None,
+                            stream=None) -> None:
+    """gdn_decode_step with the library-held workspace (no workspace argument;
+    calls on one GPU must not overlap in time)."""
+    lib = _abi.load()
+    B = slot_idx.numel()
+    Hv, dv = geom.num_v_heads, geom.head_v_dim
+    act = geom.act_dtype
+    _, host = _host_i32(slot_idx_host, B, "slot_idx_host")
+    g = geom.c()
+    _abi.check(lib.gdn_decode_step_noalloc(
+        ctypes.byref(g), ctypes.byref(w.c), ctypes.byref(pool.c),
+        _ptr(slot_idx, torch.int32, B, "slot_idx"), host, B,
+        _ptr(qkv_in, act, B * geom.channels, "qkv_in"),
+        _ptr(z, act, B * Hv * dv, "z"), _ptr(a, act, B * Hv, "a"), _ptr(b, act, B * Hv, "b"),
+        _ptr(y, act, B * Hv * dv, "y"), _ptr(o_raw, torch.float32, B * Hv * dv, "o_raw"),
         _stream(stream)))
 
 

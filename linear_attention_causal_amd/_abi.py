@@ -78,6 +78,8 @@ PROTOTYPES = {
     "gdn_decode_workspace_bytes": (ctypes.c_int, [_GP, _I32, _SZP]),
     "gdn_decode_step": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]),
+    "gdn_decode_step_noalloc": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _I32, _P, _P, _P, _P, _P,
+                                               _P, _P]),
     "gdn_prefill_chunked": (ctypes.c_int, [_GP, _WP, _PP, _P, _P, _P, _P, _P, _I32, _P, _P,
                                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "gdn_linear": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.POINTER(gdn_linear_out), _I32,

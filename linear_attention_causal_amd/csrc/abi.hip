@@ -221,6 +221,37 @@ int gdn_decode_step(const gdn_geometry* geom, const gdn_layer_weights* w,
                     "gdn_decode_step launch");
 }
 
+int gdn_decode_step_noalloc(const gdn_geometry* geom, const gdn_layer_weights* w,
+                            const gdn_state_pool* pool, const int32_t* slot_idx,
+                            const int32_t* slot_idx_host, int32_t B, const void* qkv_in,
+                            const void* z, const void* a, const void* b, void* y,
+                            float* o_raw, void* stream) {
+  GDN_TRY(check_geometry(geom));
+  GDN_TRY(check_weights(w));
+  GDN_TRY(check_pool(pool, true, true));
+  if (B < 0) return fail(GDN_E_SHAPE, "B = %d is negative", B);
+  if ((long long)B * geom->num_v_heads > (1LL << 30)) return fail(GDN_E_SHAPE, "B too large");
+  if (B == 0) return ok();
+  if (!slot_idx || !qkv_in || !z || !a || !b || !y)
+    return fail(GDN_E_NULL, "a device array is NULL");
+  if (!aligned16(qkv_in) || !aligned16(z) || !aligned16(y) || (o_raw && !aligned16(o_raw)))
+    return fail(GDN_E_ALIGN, "qkv_in, z, y, o_raw must be 16-byte aligned");
+  const size_t need = gdn::decode_workspace_bytes(*geom, B);
+  if (need > gdn::kStaticScratchBytes)
+    return fail(GDN_E_SCRATCH,
+                "gdn_decode_step_noalloc: %d rows need %zu bytes of workspace, more than the "
+                "%zu bytes the library holds; use gdn_decode_step with a workspace",
+                B, need, gdn::kStaticScratchBytes);
+  GDN_TRY(check_slots_host(slot_idx_host, B, pool->num_slots));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int rc = hip_status(gdn::static_scratch(&ws, st), "gdn_decode_step_noalloc scratch");
+  if (rc != GDN_OK) return rc;
+  return hip_status(gdn::launch_decode_step(*geom, *w, *pool, slot_idx, B, qkv_in, z, a, b, y,
+                                            o_raw, ws, st),
+                    "gdn_decode_step_noalloc launch");
+}
+
 int gdn_prefill_chunked(const gdn_geometry* geom, const gdn_layer_weights* w,
                         const gdn_state_pool* pool, const int32_t* cu_seqlens_host,
                         const int32_t* cu_seqlens_dev, const int32_t* slot_idx,

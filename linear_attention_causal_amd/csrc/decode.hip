@@ -18,6 +18,8 @@
 //   u  = beta (v - e^g kappa),   S' = e^g S + k u^T,   o = S'^T q = e^g rho + u (k.q)
 // so the kernel is one coalesced f32 read and one write of the tile, the
 // bandwidth floor of the step.
+#include <mutex>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -550,6 +552,49 @@ hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
   p.per_xcd = (int)((per + p.r - 1) / p.r * p.r);   // a (row, K-head) never straddles two XCDs
   if (g.act_dtype == GDN_BF16) return head_d<__bf16>(p, g.head_k_dim, g.conv_kernel, stream);
   return head_d<float>(p, g.head_k_dim, g.conv_kernel, stream);
+}
+
+// ------------------------------------------------------------- no-alloc step
+
+// Workspace of gdn_decode_step_noalloc: one array per GPU in the code object,
+// held until the process ends.  Host code never names it as an address (the
+// name is a host-side stand-in); it uses the per-device pointer that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device
+}  // namespace
+
+// The calling thread's current device's copy of the array, set up on the
+// first call for that device: its address taken once with the device
+// current, and the array cleared once (a fill kernel on `stream`, ahead of
+// the step; no memset node, so the clear may also be captured).
+hipError_t static_scratch(void** ptr, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    fill_zero_kernel<<<64, 256, 0, stream>>>(static_cast<u32x4*>(p), kStaticScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------- launchers

@@ -22,6 +22,11 @@ hipError_t launch_decode(const gdn_geometry& g, const gdn_layer_weights& w,
 // fits).
 size_t decode_workspace_bytes(const gdn_geometry& g, long long B);
 
+// Library-held workspace of gdn_decode_step_noalloc: size, and the current
+// device's copy (address taken and array cleared on first use per device).
+constexpr size_t kStaticScratchBytes = GDN_NOALLOC_WORKSPACE_BYTES;
+hipError_t static_scratch(void** ptr, hipStream_t stream);
+
 hipError_t launch_decode_step(const gdn_geometry& g, const gdn_layer_weights& w,
                               const gdn_state_pool& pool, const int32_t* slot_idx, int B,
                               const void* qkv_in, const void* z, const void* a, const void* b,

@@ -34,7 +34,7 @@ def host_i32(vals):
 
 def test_exports_every_declared_function():
     names = _abi.header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(_abi.PROTOTYPES) == set(names)
@@ -163,6 +163,23 @@ def test_decode_step_checks():
     assert step(g, z=None) == _abi.GDN_E_NULL
     assert step(geom(Hk=2, Hv=6, d=32), P=1 << 20, ws=None) == _abi.GDN_E_SCRATCH
     assert b"workspace" in lib.gdn_last_error()
+
+
+def test_decode_step_noalloc_checks():
+    """gdn_decode_step_noalloc validates like gdn_decode_step and rejects row
+    counts whose workspace exceeds the 1 MiB the library holds per GPU, all
+    before touching the device (every call below returns before a launch)."""
+    def step(g, B=4, z=DEV):
+        w, p = weights(), pool(64)
+        return lib.gdn_decode_step_noalloc(ctypes.byref(g), ctypes.byref(w), ctypes.byref(p),
+                                           DEV, None, B, DEV, z, DEV, DEV, DEV, None, None)
+    g = geom(Hk=16, Hv=32)
+    assert step(g, B=0) == 0
+    assert step(g, B=-1) == _abi.GDN_E_SHAPE
+    assert step(g, z=None) == _abi.GDN_E_NULL
+    assert _ws_bytes(g, 4096) == 1 << 20 and _ws_bytes(g, 4097) > 1 << 20
+    assert step(g, B=4097) == _abi.GDN_E_SCRATCH
+    assert b"1048576" in lib.gdn_last_error()
 
 
 def _prefill(cu, slots_host=None, scratch=DEV, nbytes=1 << 40, N=None):
