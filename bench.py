@@ -5,24 +5,33 @@
 Headline (`value`): batched decode at one rank's share of the heads, B = 16
 rows, Hk = 8, Hv = 16, dk = dv = 128, bf16 activations, f32 state, 64-slot
 pool.  One step = gdn_decode_step (conv update, state update and gated
-RMSNorm in one launch) for the 16 rows of one layer.  Steps rotate over 16 layer replicas (pools, weights and inputs) so
-that every step streams its state from HBM rather than from the 256 MB
-last-level cache, as consecutive layers of a model do.
+RMSNorm in one launch) for the 16 rows of one layer.  Steps rotate over 16
+layer replicas (pools, weights and inputs) so that every step streams its
+state from HBM rather than from the 256 MB last-level cache, as consecutive
+layers of a model do.  Exactly K steps run in the timed region, replayed
+from HIP graphs captured beforehand (the captured-graph decode of serving).
 
 Also reported on the same JSON line:
   roofline      the fused decode kernel: algorithmic bytes per launch / its
-                mean duration from HIP events on the launch stream, vs 8 TB/s;
-  prefill       4096-token single-sequence prefill (Hk=8, Hv=16) and the
-                8-sequence packed varlen prefill (Hk=16, Hv=32): tokens/s and
-                algorithmic MFMA fraction;
+                mean duration from HIP events on the launch stream over a
+                1024-launch graph replay, vs 8 TB/s; HBM traffic per launch
+                from the committed counter record;
+  prefill       the 4096-token single-sequence prefill (Hk=8, Hv=16) and the
+                8-sequence packed varlen prefill (Hk=16, Hv=32): median call
+                time over 100 calls, tokens/s, an HBM roofline object (the
+                whole call is HBM-bound by its algorithm) and the MFMA
+                figures (algorithmic fraction of the bf16 peak; MFMA-pipe
+                utilisation from the committed counter record);
+  serving       B = 256 rows through 48 layers (Hk=16, Hv=32, 320-slot
+                pools), 64 steps with a retire + compaction + admission
+                event after steps 16, 32 and 48; roofline of its layer launch;
   block         one decode token per row through the whole block (input
                 projections, the layer, out_proj; hidden 2048) at B = 16
                 rank-local and B = 256 full-head, with the library GEMM timed
                 beside the projection kernel;
-  serving       B = 256 rows through 48 layers (Hk=16, Hv=32, 320-slot pools)
-                with a retire + compaction event every 16 steps;
-  cpu_baseline  the f64 oracle on the host cores, on a bounded sample of the
-                headline workload.
+  cpu_baseline  the f64 oracle on the host cores for the headline workload,
+                and `cpu_baselines` for every workload, each at one thread
+                and at all the threads the oracle uses, on bounded samples.
 """
 from __future__ import annotations
 
@@ -38,9 +47,9 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN decode tokens/s + % HBM peak; chunked prefill tokens/s + % MFMA"
 HBM_PEAK = 8.0e12            # bytes/s
 BF16_PEAK = 2.5e15           # dense MFMA flop/s
-F32_MFMA_PEAK = 157.3e12     # dense f32 MFMA flop/s
 PREFILL_FLOP_PER_TOKEN_HEAD = 180_224   # chunk contractions at d = 128, L = 64
-GRAPH_PASSES = 4             # passes over the layer replicas per captured decode graph
+ROOFLINE_GRAPH = 1024        # launches per graph for the roofline's mean launch time
+LEGS = ("decode", "prefill", "block", "serving")
 
 
 def log(msg):
@@ -50,13 +59,19 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of " + ",".join(LEGS) +
+                         " (the headline decode always runs unless --prefill-only)")
+    ap.add_argument("--prefill-iters", type=int, default=100)
+    ap.add_argument("--serving-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="headline decode only (for profiler runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="wall-time budget of each oracle sample loop")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 512 MiB device copy kernel (the reference "
                          "for scaling the HBM byte counters of a profiler run)")
@@ -78,6 +93,11 @@ def _t(x, dtype):
     import numpy as np
     import torch
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
+
+
+def geometry(gdn, s):
+    return gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                        s.conv_kernel, s.act)
 
 
 class DecodeLayer:
@@ -113,99 +133,45 @@ def step_bytes(geom, B, act_bytes):
                 + 2 * Hv * dv * act_bytes + 2 * Hv * act_bytes)
 
 
-# ------------------------------------------------------------------ decode
+def prefill_bytes(geom, T, N, act_bytes):
+    """Algorithmic bytes of one prefill call: per token the fused input (C),
+    z and y (Hv dv each) and a, b (Hv each); per sequence the recurrent
+    state read and written and the conv window (K-1 columns read, K written)."""
+    C, Hv, dk, dv, K = (geom.channels, geom.num_v_heads, geom.head_k_dim, geom.head_v_dim,
+                        geom.conv_kernel)
+    per_token = (C + 2 * Hv * dv + 2 * Hv) * act_bytes
+    per_seq = 8 * Hv * dk * dv + (2 * K - 1) * C * act_bytes
+    return T * per_token + N * per_seq
 
 
-def bench_decode(args):
-    """The headline step, replayed from a HIP graph (one graph = one pass over
-    the layer replicas), as the pages' serving path replays captured decode
-    steps.  An eager (one Python launch per step) figure is reported beside it."""
-    import numpy as np
+def capture(fn):
+    """Capture fn(stream) on a side stream into a HIP graph (nothing runs)."""
     import torch
-
-    import linear_attention_causal_amd as gdn
-    import workloads as wl
-
-    work = wl.decode_batch(seed=0)
-    s = work.shape
-    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
-                        s.conv_kernel, s.act)
-    act = torch.bfloat16
-    B = len(work.data["slot_idx"])
-    R = args.replicas
-    layers = [DecodeLayer(gdn, geom, work.data, act) for _ in range(R)]
-    y = torch.empty(B, geom.num_v_heads, geom.head_v_dim, device="cuda", dtype=act)
-    ws = gdn.decode_workspace(geom, B)
-
-    def step(i, stream):
-        L = layers[i % R]
-        gdn.gdn_decode_step(geom, L.w, L.pool, L.slot, L.x, L.z, L.a, L.b, y, ws, stream=stream)
-
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        step(i, stream)
-    torch.cuda.synchronize()
-    # eager: one Python-side launch per step
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, stream)
-    torch.cuda.synchronize()
-    eager_dt = time.perf_counter() - t0
-
-    # graph: G = GRAPH_PASSES * R steps (passes over the replicas) captured
-    # once, replayed; more steps per graph spread the replay's own launch cost
-    G = GRAPH_PASSES * R
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            for i in range(G):
-                step(i, side)
+            fn(side)
     stream.wait_stream(side)
-    for _ in range(max(1, args.warmup // G)):
-        graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, args.steps // G)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    t0 = time.perf_counter()
-    for k in range(reps):
-        evs[k][0].record(stream)
-        graph.replay()
-        evs[k][1].record(stream)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    nsteps = reps * G
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / G
-    per_launch = step_bytes(geom, B, 2)
-    achieved = per_launch / (launch_ms * 1e-3)
-    rec = recorded_traffic()
-    return dict(
-        tokens_per_s=B * nsteps / dt, ms_per_step=dt * 1e3 / nsteps, steps=nsteps, B=B,
-        workload=work.name, geom=geom,
-        eager={"tokens_per_s": B * args.steps / eager_dt,
-               "ms_per_step": eager_dt * 1e3 / args.steps},
-        roofline={"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
-                  "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                  "traffic": rec["hbm_bytes_per_launch"] if rec else None,
-                  "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
-                  "kernel": "gdn::decode_head_kernel<__bf16, 128, 4, 1>",
-                  "bytes_per_launch": per_launch, "mean_launch_us": launch_ms * 1e3,
-                  "timing": f"HIP events around graph replays of {G} back-to-back launches "
-                            f"({GRAPH_PASSES} passes over {R} replicas)"},
-        step_hbm_frac=per_launch / (dt / nsteps) / HBM_PEAK)
+    return graph
+
+
+# ------------------------------------------------------------------ records
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_step_b16_hk8_hv16_d128_traffic.md")
-TRAFFIC_SOURCES = ("linear_attention_causal_amd/csrc/decode.hip",
-                   "linear_attention_causal_amd/csrc/gdn_device.hpp")
+SERVING_RECORD = os.path.join(ROOT, "profiles", "decode_step_b256_hk16_hv32_d128_traffic.md")
+DECODE_SOURCES = ("linear_attention_causal_amd/csrc/decode.hip",
+                  "linear_attention_causal_amd/csrc/gdn_device.hpp")
 MFMA_RECORD = os.path.join(ROOT, "profiles", "prefill_t4096_varlen8_d128.md")
-MFMA_SOURCES = ("linear_attention_causal_amd/csrc/prefill.hip",
-                "linear_attention_causal_amd/csrc/gdn_device.hpp")
+PREFILL_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "prefill_t4096_varlen8_d128_traffic.md")
+PREFILL_SOURCES = ("linear_attention_causal_amd/csrc/prefill.hip",
+                   "linear_attention_causal_amd/csrc/gdn_device.hpp")
 
 
-def kernel_source_digest(sources=TRAFFIC_SOURCES):
+def kernel_source_digest(sources):
     import hashlib
     h = hashlib.sha256()
     for rel in sources:
@@ -231,18 +197,21 @@ def read_record(path, sources):
     return rec
 
 
-def recorded_traffic():
-    """HBM bytes per decode launch from the committed counter record (FETCH_SIZE
-    and WRITE_SIZE passes, each scaled by the same counter's reading on a plain
-    copy of known size)."""
-    return read_record(TRAFFIC_RECORD, TRAFFIC_SOURCES)
+def recorded_traffic(path, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed counter record (FETCH_SIZE and
+    WRITE_SIZE passes, each scaled by the same counter's reading on a plain
+    copy of known size), or None."""
+    rec = read_record(path, DECODE_SOURCES)
+    return rec.get(key) if rec else None
 
 
-def recorded_mfma_util(workload):
-    """MFMA-pipe utilisation (percent, kernel-time weighted over a prefill call)
-    from the committed counter record, or None."""
-    rec = read_record(MFMA_RECORD, MFMA_SOURCES)
-    return rec["mfma_pipe_util_pct"].get(workload) if rec else None
+def recorded_prefill(workload):
+    """(MFMA-pipe utilisation percent, HBM bytes per call) of a prefill workload
+    from the committed counter records, each None when absent or stale."""
+    m = read_record(MFMA_RECORD, PREFILL_SOURCES)
+    t = read_record(PREFILL_TRAFFIC_RECORD, PREFILL_SOURCES)
+    return (m["mfma_pipe_util_pct"].get(workload) if m else None,
+            t["hbm_bytes_per_call"].get(workload) if t else None)
 
 
 def calibration_copy(nbytes=512 << 20, reps=4):
@@ -269,6 +238,100 @@ def calibration_gemm(n=8192, reps=4):
     log(f"[bench] calibration gemm: bf16 {n}^3, {reps} launches")
 
 
+# ------------------------------------------------------------------ decode
+
+
+def bench_decode(args):
+    """The headline step.  Exactly args.steps launches run in the timed
+    region, replayed from HIP graphs (one of min(K, 1024) launches replayed
+    K // 1024 times, plus one of the remainder), bracketed by a device
+    synchronisation on both sides; the wall time between gives `value`.
+    The roofline's mean launch duration comes from HIP events on the replay
+    stream around separate replays of a 1024-launch graph.  An eager (one
+    Python launch per step) figure is reported beside it."""
+    import numpy as np
+    import torch
+
+    import linear_attention_causal_amd as gdn
+    import workloads as wl
+
+    work = wl.decode_batch(seed=0)
+    s = work.shape
+    geom = geometry(gdn, s)
+    act = torch.bfloat16
+    B = len(work.data["slot_idx"])
+    R = args.replicas
+    K = max(1, args.steps)
+    layers = [DecodeLayer(gdn, geom, work.data, act) for _ in range(R)]
+    y = torch.empty(B, geom.num_v_heads, geom.head_v_dim, device="cuda", dtype=act)
+    ws = gdn.decode_workspace(geom, B)
+
+    def step(i, stream):
+        L = layers[i % R]
+        gdn.gdn_decode_step(geom, L.w, L.pool, L.slot, L.x, L.z, L.a, L.b, y, ws, stream=stream)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    # eager: one Python-side launch per step (not the headline)
+    n_eager = max(K, 64)
+    t0 = time.perf_counter()
+    for i in range(n_eager):
+        step(i, stream)
+    torch.cuda.synchronize()
+    eager_dt = time.perf_counter() - t0
+
+    # timed region: exactly K launches from captured graphs
+    G = min(K, ROOFLINE_GRAPH)
+    full, rem = divmod(K, G)
+    g_full = capture(lambda st: [step(i, st) for i in range(G)])
+    g_rem = capture(lambda st: [step(full * G + i, st) for i in range(rem)]) if rem else None
+    g_full.replay()                      # untimed: first replay uploads the graph
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    # roofline: mean launch duration over replays of a 1024-launch graph
+    g_roof = capture(lambda st: [step(i, st) for i in range(ROOFLINE_GRAPH)])
+    g_roof.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(4)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        g_roof.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / ROOFLINE_GRAPH
+    per_launch = step_bytes(geom, B, 2)
+    achieved = per_launch / (launch_ms * 1e-3)
+    return dict(
+        tokens_per_s=B * K / dt, ms_per_step=dt * 1e3 / K, steps=K, B=B,
+        workload=work.name, geom=geom,
+        eager={"tokens_per_s": B * n_eager / eager_dt, "ms_per_step": eager_dt * 1e3 / n_eager,
+               "steps": n_eager},
+        timed_region={"launches": K, "graphs": f"{full} x {G} launches" +
+                      (f" + 1 x {rem}" if rem else ""), "wall_s": dt},
+        roofline={"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                  "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                  "traffic": recorded_traffic(TRAFFIC_RECORD),
+                  "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+                  "kernel": "gdn::decode_head_kernel<__bf16, 128, 4>",
+                  "bytes_per_launch": per_launch, "mean_launch_us": launch_ms * 1e3,
+                  "timing": f"HIP events on the launch stream around 4 replays of a graph of "
+                            f"{ROOFLINE_GRAPH} back-to-back launches ({ROOFLINE_GRAPH // R} "
+                            f"passes over {R} replicas)"},
+        step_hbm_frac=per_launch / (dt / K) / HBM_PEAK)
+
+
 # ------------------------------------------------------------------ prefill
 
 
@@ -279,8 +342,7 @@ def bench_prefill(work, iters, replicas):
     import linear_attention_causal_amd as gdn
 
     s, d = work.shape, work.data
-    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
-                        s.conv_kernel, s.act)
+    geom = geometry(gdn, s)
     act = torch.bfloat16
     cu = d["cu_seqlens"]
     T, N = int(cu[-1]), len(cu) - 1
@@ -320,23 +382,33 @@ def bench_prefill(work, iters, replicas):
     torch.cuda.synchronize()
     ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
     flops = PREFILL_FLOP_PER_TOKEN_HEAD * T * geom.num_v_heads * (geom.head_k_dim / 128) ** 2
-    return {"workload": work.name, "tokens": T, "sequences": N, "ms_per_call": ms,
-            "tokens_per_s": T / (ms * 1e-3),
-            "algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
-            "mfma_frac_of_bf16_peak": flops / (ms * 1e-3) / BF16_PEAK,
-            "mfma_frac_of_f32_peak": flops / (ms * 1e-3) / F32_MFMA_PEAK,
-            "mfma_pipe_util_pct": recorded_mfma_util(work.name),
-            "mfma_pipe_util_source": "rocprofv3 MfmaUtil, kernel-time weighted over the call "
-                                     "(committed prefill profile record; null once the "
-                                     "kernels change)",
-            "mfma_dtype": "bf16 x3 (hi/lo split operands, f32 accumulate)", "kernels": 4}
+    nbytes = prefill_bytes(geom, T, N, 2)
+    util, traffic = recorded_prefill(work.name)
+    return {"workload": work.name, "tokens": T, "sequences": N, "calls": iters,
+            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": nbytes / (ms * 1e-3) / HBM_PEAK, "traffic": traffic,
+                         "traffic_unit": "HBM bytes per call (scaled FETCH_SIZE + WRITE_SIZE "
+                                         "over the call's kernels)",
+                         "bytes_per_call": nbytes,
+                         "timing": f"median over {iters} calls, HIP events on the launch stream"},
+            "mfma": {"algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
+                     "algorithmic_frac_of_bf16_peak": flops / (ms * 1e-3) / BF16_PEAK,
+                     "flop_per_call": flops,
+                     "pipe_util_pct": util,
+                     "pipe_util_source": "rocprofv3 MfmaUtil, kernel-time weighted over the "
+                                         "call (committed prefill profile record; null once "
+                                         "the kernels change)",
+                     "dtype": "bf16 x3 on the state path (hi/lo split operands, f32 "
+                              "accumulate), x1 on the output-only products"}}
 
 
 # ------------------------------------------------------------------ block
 
 
 def _graph_us(fn, R, warm=2, reps=20):
-    """Mean device time (us) of one of R back-to-back calls fn(r), captured
+    """Median device time (us) of one of R back-to-back calls fn(r), captured
     once in a HIP graph and replayed, from HIP events on the replay stream."""
     import numpy as np
     import torch
@@ -379,8 +451,7 @@ def bench_block(B, shape, P, replicas):
 
     work = wl.decode_block(seed=0, B=B, P=P, s=shape)
     s, d = work.shape, work.data
-    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
-                        s.conv_kernel, s.act)
+    geom = geometry(gdn, s)
     bf = torch.bfloat16
     H = d["hidden"].shape[1]
     C, Hv, vd = s.channels, s.num_v_heads, s.num_v_heads * s.head_v_dim
@@ -463,11 +534,15 @@ def bench_block(B, shape, P, replicas):
 # ------------------------------------------------------------------ serving
 
 
-def bench_serving(steps=32, layers=48, B=256, P=320):
-    """B rows through `layers` layers per step; after every 16 steps a seeded
-    half of the rows retire, survivors are compacted across all layers and
-    new rows are admitted (zero state).  Pools and inputs are drawn on the
-    device from a seeded generator."""
+def bench_serving(steps=64, layers=48, B=256, P=320, event_every=16):
+    """B rows through `layers` layers per step, the layer launches of a step
+    captured once as a HIP graph and replayed; after every `event_every`
+    steps a seeded half of the rows retire, the survivors are compacted into
+    the prefix across all layers (gdn_state_compact) and as many new rows are
+    admitted behind them with zeroed state (recurrent and conv), the device
+    slot index rewritten in place.  Pools and inputs are drawn on the device
+    from a seeded generator (their values do not affect timing; this
+    schedule's parity is tested at full head count with host-drawn pools)."""
     import numpy as np
     import torch
 
@@ -475,8 +550,7 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
     import workloads as wl
 
     s = wl.FULL_HEADS
-    geom = gdn.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
-                        s.conv_kernel, s.act)
+    geom = geometry(gdn, s)
     act = torch.bfloat16
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
@@ -500,9 +574,7 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
     y = torch.empty(B, s.num_v_heads, s.head_v_dim, device="cuda", dtype=act)
     stream = torch.cuda.current_stream()
     pools = [L["pool"] for L in Ls]
-    compact_ms = []
-    # device-resident slot index: the captured step reads it, a retire event
-    # rewrites it in place
+    # device-resident slot index: the captured step reads it, an event rewrites it in place
     slot_d = _t(live, torch.int32)
     ws = gdn.decode_workspace(geom, B)
 
@@ -510,100 +582,242 @@ def bench_serving(steps=32, layers=48, B=256, P=320):
         for L in Ls:
             gdn.gdn_decode_step(geom, L["w"], L["pool"], slot_d, x, z, a, b, y, ws, stream=st)
 
-    graph = None
+    events = []
 
-    def run(nsteps, live, use_graph):
-        for t in range(nsteps):
-            if t > 0 and t % 16 == 0:
-                keep, new_slots, src, dst = wl.retire_plan(rng, live, P)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                if src.size:
-                    gdn.gdn_state_compact(geom, pools, src, dst, _t(src, torch.int32),
-                                          _t(dst, torch.int32), stream=stream)
-                e1.record(stream)
-                compact_ms.append((e0, e1, int(src.size)))
-                admitted = np.arange(len(new_slots), len(new_slots) + (len(live) - len(new_slots)),
-                                     dtype=np.int32)
-                live = np.concatenate([new_slots, admitted]).astype(np.int32)
-                slot_d.copy_(torch.from_numpy(live))
-            if use_graph:
-                graph.replay()
-            else:
-                layer_pass(stream)
+    def event(live):
+        keep, new_slots, src, dst = wl.retire_plan(rng, live, P)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        if src.size:
+            gdn.gdn_state_compact(geom, pools, src, dst, _t(src, torch.int32),
+                                  _t(dst, torch.int32), stream=stream)
+        e1.record(stream)
+        n_keep = len(new_slots)
+        n_new = len(live) - n_keep
+        for L in Ls:                      # admitted rows start from zero state
+            L["rec"][n_keep:n_keep + n_new].zero_()
+            L["conv"][n_keep:n_keep + n_new].zero_()
+        e2.record(stream)
+        events.append((e0, e1, e2, int(src.size), n_new))
+        live = np.concatenate([new_slots, np.arange(n_keep, n_keep + n_new)]).astype(np.int32)
+        slot_d.copy_(torch.from_numpy(live))
         return live
 
-    live = run(2, live, False)
-    torch.cuda.synchronize()
-    compact_ms.clear()
-    t0 = time.perf_counter()
-    live = run(steps, live, False)
-    torch.cuda.synchronize()
-    eager_dt = time.perf_counter() - t0
-    compact_ms.clear()
-    # one HIP graph per step: the 48 layer launches captured once
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            layer_pass(side)
-    stream.wait_stream(side)
+    graph = capture(layer_pass)
     graph.replay()
     torch.cuda.synchronize()
+    step_ev = []
     t0 = time.perf_counter()
-    run(steps, live, True)
+    for t in range(steps):
+        if t > 0 and t % event_every == 0:
+            live = event(live)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        step_ev.append((e0, e1))
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    cms = [a_.elapsed_time(b_) for a_, b_, _ in compact_ms]
-    moved = [n for _, _, n in compact_ms]
-    per_step = layers * step_bytes(geom, B, 2)
+    step_ms = [a_.elapsed_time(b_) for a_, b_ in step_ev]
+    launch_us = float(np.median(step_ms)) * 1e3 / layers
+    per_launch = step_bytes(geom, B, 2)
+    per_step = layers * per_launch
     return {"workload": f"decode_b{B}_hk16_hv32_d128_p{P}_x{layers}layers",
-            "launch": "HIP graph of the 48 layer launches per step, replayed",
-            "tokens_per_s": B * steps / dt, "ms_per_step": dt * 1e3 / steps,
+            "launch": f"HIP graph of the {layers} layer launches per step, replayed",
+            "steps": steps, "tokens_per_s": B * steps / dt, "ms_per_step": dt * 1e3 / steps,
             "hbm_frac_algorithmic": per_step * steps / dt / HBM_PEAK,
-            "eager_tokens_per_s": B * steps / eager_dt,
-            "compaction_events": len(cms), "compaction_ms": cms, "compaction_pairs": moved,
-            "steps": steps}
+            "events": [{"after_step": event_every * (i + 1), "pairs_moved": n,
+                        "admitted": adm, "compaction_ms": e0.elapsed_time(e1),
+                        "admission_zeroing_ms": e1.elapsed_time(e2)}
+                       for i, (e0, e1, e2, n, adm) in enumerate(events)],
+            "roofline": {"bound": "hbm", "achieved": per_launch / (launch_us * 1e-6) / 1e9,
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": per_launch / (launch_us * 1e-6) / HBM_PEAK,
+                         "traffic": recorded_traffic(SERVING_RECORD),
+                         "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+                         "kernel": "gdn::decode_head_kernel<__bf16, 128, 4>",
+                         "bytes_per_launch": per_launch, "mean_launch_us": launch_us,
+                         "timing": f"median over the {steps} replayed steps of HIP events on "
+                                   f"the launch stream, / {layers} launches"}}
 
 
 # ------------------------------------------------------------------ CPU oracle
 
 
-def cpu_baseline(seconds):
-    """The f64 oracle (as it stands) on the host cores: decode steps of the
-    headline workload (16 rows, Hk=8, Hv=16, d=128), repeated until about
-    `seconds` of wall time has passed."""
+def host_info():
+    import platform
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "cpus_available": avail}
+
+
+def _rate(fn, units, budget):
+    """units per second of fn() repeated for about `budget` seconds (at least once)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget:
+            return units * n / dt, n, dt
+
+
+def cpu_baselines(budget, gpu=None):
+    """The oracle as it stands (f64, C, one thread per independent (sequence
+    or row, V-head) unit) on bounded samples of every workload, at one thread
+    and at all the threads it uses.  Returns (headline entry, list)."""
     import numpy as np
 
     import oracle
     import workloads as wl
 
-    work = wl.decode_batch(seed=0)
-    s, d = work.shape, work.data
-    og = oracle.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
-                         s.conv_kernel)
-    ow = oracle.Weights(d["weights"]["conv_w"], d["weights"]["A_log"], d["weights"]["dt_bias"],
-                        d["weights"]["norm_w"])
-    S, W = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
-    B = len(d["slot_idx"])
-    def run(threads, budget):
-        n = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget:
-            oracle.pool_run(og, ow, S, W, np.arange(B + 1), d["slot_idx"], d["x"], d["z"],
-                            d["a"], d["b"], nthreads=threads)
-            n += 1
-        return n, time.perf_counter() - t0
+    info = host_info()
+    nthr = oracle.default_threads()
+    gpu = gpu or {}
 
-    threads = oracle.default_threads()
-    n, dt = run(threads, seconds)
-    n1, dt1 = run(1, max(2.0, seconds / 4))
-    return {"value": B * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "single_thread_value": B * n1 / dt1,
-            "sample": f"{n} decode steps of the headline workload (16 rows x 16 V-heads, "
-                      f"d=128) in {dt:.1f} s, f64, one thread per (row, V-head) unit; "
-                      f"single thread: {n1} steps in {dt1:.1f} s"}
+    def og(s):
+        return oracle.Geometry(s.num_k_heads, s.num_v_heads, s.head_k_dim, s.head_v_dim,
+                               s.conv_kernel)
+
+    def ow(w):
+        return oracle.Weights(w["conv_w"], w["A_log"], w["dt_bias"], w["norm_w"])
+
+    out = []
+
+    def entry(name, unit, fns, sample, gpu_val=None):
+        """fns: threads -> (callable, units per call)."""
+        res = {"workload": name, "unit": unit, "sample": sample}
+        for key, thr in (("all_threads", nthr), ("one_thread", 1)):
+            fn, units = fns(thr)
+            v, n, dt = _rate(fn, units, budget)
+            res[key] = {"value": v, "threads": thr, "calls": n, "seconds": dt}
+        if gpu_val is not None:
+            res["gpu_value"] = gpu_val
+            res["gpu_over_oracle_all_threads"] = gpu_val / res["all_threads"]["value"]
+        out.append(res)
+        log(f"[bench] oracle {name}: {res['all_threads']['value']:.4g} {unit} "
+            f"({nthr} threads), {res['one_thread']['value']:.4g} (1 thread)")
+        return res
+
+    # tiny f32 layer: the whole workload (64-token prefill + 8 decode steps)
+    wk = wl.tiny(seed=0)
+    d = wk.data
+    g1, w1 = og(wk.shape), ow(d["weights"])
+
+    def tiny_fns(thr):
+        def f():
+            S, W = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
+            pre = d["prefill"]
+            oracle.pool_run(g1, w1, S, W, d["cu_seqlens"], d["slot_idx"], pre["x"], pre["z"],
+                            pre["a"], pre["b"], nthreads=thr)
+            for st in d["steps"]:
+                oracle.pool_run(g1, w1, S, W, [0, 1], d["slot_idx"], st["x"], st["z"], st["a"],
+                                st["b"], nthreads=thr)
+        return f, 64 + len(d["steps"])
+    entry(wk.name, "tokens/s", tiny_fns, "the whole workload: 64-token prefill then 8 "
+          "decode steps, Hk=2, Hv=4, d=32")
+
+    # headline: decode steps of 16 rows
+    wk = wl.decode_batch(seed=0)
+    d = wk.data
+    g2, w2 = og(wk.shape), ow(d["weights"])
+    S2, W2 = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
+    B = len(d["slot_idx"])
+
+    def dec_fns(thr):
+        return (lambda: oracle.pool_run(g2, w2, S2, W2, np.arange(B + 1), d["slot_idx"], d["x"],
+                                        d["z"], d["a"], d["b"], nthreads=thr)), B
+    head = entry(wk.name, "tokens/s", dec_fns, "repeated decode steps of the 16 rows "
+                 "(Hk=8, Hv=16, d=128), one step = 16 tokens", gpu.get("decode"))
+
+    # 4096-token prefill: all heads; one thread on the first 512 tokens
+    wk = wl.prefill_single(seed=0)
+    d = wk.data
+    g3, w3 = og(wk.shape), ow(d["weights"])
+
+    def pre_fns(thr):
+        T = 4096 if thr > 1 else 512
+        S0, W0 = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
+        return (lambda: oracle.sequences(g3, w3, [0, T], d["x"][:T], d["z"][:T], d["a"][:T],
+                                         d["b"][:T], S0, W0, nthreads=thr)), T
+    entry(wk.name, "tokens/s", pre_fns, "all threads: the whole 4096-token call; one thread: "
+          "its first 512 tokens (the token loop's cost per token is constant)",
+          gpu.get(wk.name))
+
+    # 8-sequence varlen prefill: the first tokens of every sequence
+    wk = wl.prefill_varlen(seed=0)
+    d = wk.data
+    g5, w5 = og(wk.shape), ow(d["weights"])
+    cu = d["cu_seqlens"]
+
+    def var_fns(thr):
+        n = 512 if thr > 1 else 32
+        lens = [min(n, int(cu[i + 1] - cu[i])) for i in range(len(cu) - 1)]
+        idx = np.concatenate([np.arange(cu[i], cu[i] + m) for i, m in enumerate(lens)])
+        cu_s = np.concatenate([[0], np.cumsum(lens)])
+        S0, W0 = d["rec"].astype(np.float64), d["conv"].astype(np.float64)
+        return (lambda: oracle.sequences(g5, w5, cu_s, d["x"][idx], d["z"][idx], d["a"][idx],
+                                         d["b"][idx], S0, W0, nthreads=thr)), idx.size
+    entry(wk.name, "tokens/s", var_fns, "the first 512 tokens (or all, if fewer) of each of "
+          "the 8 sequences with all threads, the first 32 with one; Hk=16, Hv=32, d=128, "
+          "with their initial states", gpu.get(wk.name))
+
+    # serving step: 256 rows x 48 layers + one compaction event; sampled on
+    # whole layer-steps of one layer's pool and one layer's compaction, scaled
+    s4 = wl.FULL_HEADS
+    rng = np.random.default_rng(0)
+    w4 = ow(wl.layer_weights(rng, s4))
+    g4 = og(s4)
+    P4, B4, L4 = 320, 256, 48
+    S4 = (rng.standard_normal((P4, s4.num_v_heads, s4.head_k_dim, s4.head_v_dim)) * 0.1)
+    W4 = rng.standard_normal((P4, s4.conv_kernel, s4.channels)) * 0.1
+    live = rng.choice(P4, B4, replace=False).astype(np.int32)
+    inp = wl.token_inputs(rng, s4, B4)
+    _, _, src, dst = wl.retire_plan(rng, live, P4)
+
+    def srv_fns(thr):
+        rows = B4 if thr > 1 else 16
+        def f():
+            oracle.pool_run(g4, w4, S4, W4, np.arange(rows + 1), live[:rows], inp["x"][:rows],
+                            inp["z"][:rows], inp["a"][:rows], inp["b"][:rows], nthreads=thr)
+        return f, rows
+    srv = entry(f"decode_b{B4}_hk16_hv32_d128_p{P4}_x{L4}layers", "tokens/s (one layer)",
+                srv_fns, "layer-steps of one 320-slot pool (all 256 rows with all threads, 16 "
+                "rows with one); a 48-layer step costs 48 of them, so its tokens/s is this "
+                "value / 48, reported as `value_48_layers`", None)
+    for key in ("all_threads", "one_thread"):
+        srv[key]["value_48_layers"] = srv[key]["value"] / L4
+    t0 = time.perf_counter()
+    oracle.compact(g4, S4, W4, src, dst)
+    srv["compaction_event_s"] = {"one_layer": time.perf_counter() - t0,
+                                 "pairs": int(src.size), "layers_scaled": L4}
+    srv["compaction_event_s"]["all_layers"] = srv["compaction_event_s"]["one_layer"] * L4
+    if gpu.get("serving") is not None:
+        srv["gpu_value"] = gpu["serving"]
+        srv["gpu_over_oracle_all_threads"] = gpu["serving"] / srv["all_threads"]["value_48_layers"]
+    del S4, W4
+
+    hv = head["all_threads"]
+    line = {"value": hv["value"], "unit": "tokens/s", "cores": hv["threads"], "kind": "oracle",
+            "single_thread_value": head["one_thread"]["value"],
+            "sample": f"{hv['calls']} decode steps of the headline workload (16 rows x 16 "
+                      f"V-heads, d=128) in {hv['seconds']:.1f} s, f64, {hv['threads']} threads "
+                      f"(one per (row, V-head) unit, at most 16); one thread: "
+                      f"{head['one_thread']['calls']} steps",
+            **info}
+    return line, out
 
 
 def main():
@@ -615,23 +829,29 @@ def main():
     import torch
 
     import linear_attention_causal_amd as gdn
+    import workloads as wl
 
     gdn.library()
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    legs = set(args.legs.split(",")) if not args.no_extras else set()
+    bad = legs - set(LEGS)
+    if bad:
+        print(f"unknown legs {sorted(bad)}", file=sys.stderr)
+        sys.exit(2)
+    if args.calibration_copy:
+        calibration_copy()
+    if args.calibration_gemm:
+        calibration_gemm()
     if args.prefill_only:
-        import workloads as wl
-        if args.calibration_gemm:
-            calibration_gemm()
-        out = [bench_prefill(wl.prefill_single(seed=0), iters=10, replicas=6)]
+        out = [bench_prefill(wl.prefill_single(seed=0), args.prefill_iters, replicas=6)]
         torch.cuda.empty_cache()
-        out.append(bench_prefill(wl.prefill_varlen(seed=0), iters=5, replicas=1))
+        out.append(bench_prefill(wl.prefill_varlen(seed=0), args.prefill_iters, replicas=1))
         print(json.dumps({"prefill": out}), flush=True)
         return
     if args.block_only:
-        import workloads as wl
         out = [bench_block(16, wl.RANK_LOCAL, 64, args.replicas)]
         torch.cuda.empty_cache()
         out.append(bench_block(256, wl.FULL_HEADS, 320, 4))
@@ -639,10 +859,7 @@ def main():
         return
     log("[bench] decode headline")
     dec = bench_decode(args)
-    if args.calibration_copy:
-        calibration_copy()
-    if args.calibration_gemm:
-        calibration_gemm()
+    torch.cuda.empty_cache()
     line = {
         "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": dec["steps"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
@@ -653,31 +870,37 @@ def main():
                    "activations": "bf16", "state": "f32",
                    "cold_cache": f"{args.replicas} rotating layer replicas",
                    "launch": "HIP graph replay"},
+        "timed_region": dec["timed_region"],
         "eager": dec["eager"],
         "step_hbm_frac_algorithmic": dec["step_hbm_frac"],
         "roofline": dec["roofline"],
     }
-    if not args.no_extras:
-        import workloads as wl
+    gpu_vals = {"decode": dec["tokens_per_s"]}
+    if "prefill" in legs:
         log("[bench] prefill t4096")
-        pre = [bench_prefill(wl.prefill_single(seed=0), iters=10, replicas=6)]
+        pre = [bench_prefill(wl.prefill_single(seed=0), args.prefill_iters, replicas=6)]
         torch.cuda.empty_cache()
         log("[bench] prefill varlen8")
-        pre.append(bench_prefill(wl.prefill_varlen(seed=0), iters=5, replicas=1))
+        pre.append(bench_prefill(wl.prefill_varlen(seed=0), args.prefill_iters, replicas=1))
         torch.cuda.empty_cache()
         line["prefill"] = pre
+        for p in pre:
+            gpu_vals[p["workload"]] = p["tokens_per_s"]
+    if "block" in legs:
         log("[bench] decode block b16")
         line["block"] = [bench_block(16, wl.RANK_LOCAL, 64, args.replicas)]
         torch.cuda.empty_cache()
         log("[bench] decode block b256")
         line["block"].append(bench_block(256, wl.FULL_HEADS, 320, 4))
         torch.cuda.empty_cache()
+    if "serving" in legs:
         log("[bench] serving 48 layers")
-        line["serving"] = bench_serving()
+        line["serving"] = bench_serving(steps=args.serving_steps)
+        gpu_vals["serving"] = line["serving"]["tokens_per_s"]
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline"], line["cpu_baselines"] = cpu_baselines(args.cpu_seconds, gpu_vals)
     print(json.dumps(line), flush=True)
 
 
