@@ -275,6 +275,12 @@ int gdn_prefill_chunked(const gdn_geometry* geom, const gdn_layer_weights* w,
     max_len = std::max(max_len, len);
   }
   const long long T = cu_seqlens_host[N];
+  // per-chunk launches have one workgroup of 256 threads per (chunk, V-head)
+  // along x: keep their work-item counts within a dispatch's 32-bit size
+  const long long chunks_x = N <= 64 ? (T + 63) / 64 + N : (max_len + 63) / 64;
+  if ((chunks_x + 8) * geom->num_v_heads * 256 >= (1LL << 32))
+    return fail(GDN_E_SHAPE, "too many tokens for one call (%lld chunks x %d V-heads)", chunks_x,
+                geom->num_v_heads);
   GDN_TRY(check_slots_host(slot_idx_host, N, pool->num_slots));
   if (T > 0) {
     if (!qkv_in || !z || !a || !b || !y) return fail(GDN_E_NULL, "a device array is NULL");

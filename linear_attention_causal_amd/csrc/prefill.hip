@@ -157,6 +157,7 @@ struct PrefillParams {
   int32_t inl_cu[kInlineSeqs + 1];
   int32_t inl_cb[kInlineSeqs + 1];
   int N, Hk, Hv, C, num_slots, r;
+  int max_chunks;       // chunks of the longest sequence
   float l2eps, rmseps, scale;
 };
 
@@ -187,17 +188,20 @@ __device__ __forceinline__ size_t chunk_base_of(const PrefillParams& p, int n) {
 // mostly empty workgroups that still read their sequence's bounds); n is
 // the last sequence whose first chunk is at or before x.  Otherwise x is
 // the chunk and y the sequence.
+__device__ __forceinline__ void chunk_at(const PrefillParams& p, int g, int& n, int& c) {
+  int lo = 0, hi = p.N;   // inl_cb[lo] <= g < inl_cb[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.inl_cb[mid] <= g) lo = mid;
+    else hi = mid;
+  }
+  n = lo;
+  c = g - p.inl_cb[lo];
+}
+
 __device__ __forceinline__ void chunk_of(const PrefillParams& p, int& n, int& c) {
   if (p.inl) {
-    const int g = blockIdx.x;
-    int lo = 0, hi = p.N;   // inl_cb[lo] <= g < inl_cb[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.inl_cb[mid] <= g) lo = mid;
-      else hi = mid;
-    }
-    n = lo;
-    c = g - p.inl_cb[lo];
+    chunk_at(p, blockIdx.x, n, c);
   } else {
     c = blockIdx.x;
     n = blockIdx.y;
@@ -685,16 +689,31 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
   float* sT = sAT + kL * LDL;
   float* sVt = sAT;
 
+  // Block x -> unit (chunk, K-head) = (x / (8 r)) * 8 + x % 8 and V-head
+  // m r + (x / 8) % r: the r workgroups of a unit get ids 8 apart, so they
+  // are dispatched together onto one XCD and read the unit's K K^T, Q K^T
+  // and k_hat^T fragments through one L2.  Chunks run along x (all real
+  // chunks when the prefix travels with the launch, else one sequence's
+  // chunk slots per y).
+  const int per = 8 * p.r, xg = blockIdx.x / per, xr = blockIdx.x - xg * per;
+  const int unit = xg * 8 + (xr & 7);
+  const int cx = p.inl ? p.inl_cb[p.N] : p.max_chunks;
+  if (unit >= cx * p.Hk) return;
+  const int m = unit % p.Hk;
+  const int h = m * p.r + (xr >> 3);
   int n, c;
-  chunk_of(p, n, c);
-  const int h = blockIdx.z;
+  if (p.inl) {
+    chunk_at(p, unit / p.Hk, n, c);
+  } else {
+    n = blockIdx.y;
+    c = unit / p.Hk;
+  }
   const SeqInfo si = seq_info(p, n);
   const int t0 = c * kL;
   if (si.slot < 0 || t0 >= si.len) return;
   const int nc = min(kL, si.len - t0);
   const long long tok0 = si.begin + t0;
   const size_t g = chunk_base_of(p, n) + c;
-  const int m = h / p.r;
   const size_t gh = g * p.Hv + h, gk = g * p.Hk + m;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
@@ -1359,7 +1378,9 @@ static hipError_t prefill_run(const PrefillParams& p, int max_chunks, hipStream_
   const dim3 chunks = p.inl ? dim3(p.inl_cb[p.N], 1) : dim3(max_chunks, p.N);
   if (max_chunks > 0) {
     prefill_qk_kernel<Act, D, K><<<dim3(chunks.x, chunks.y, p.Hk), kNT, 0, st>>>(p);
-    prefill_wy_kernel<Act, D, K><<<dim3(chunks.x, chunks.y, p.Hv), kNT, 0, st>>>(p);
+    const long long units = (long long)chunks.x * p.Hk;   // per y
+    prefill_wy_kernel<Act, D, K><<<dim3((unsigned)((units + 7) / 8 * 8 * p.r), chunks.y), kNT, 0,
+                                   st>>>(p);
   }
   switch (state_col_blocks(p.N, p.Hv, D)) {
     case 1: launch_state<Act, D, K, 1>(p, st); break;
@@ -1442,6 +1463,7 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
   p.rmseps = g.rmsnorm_eps;
   p.scale = g.scale > 0.f ? g.scale : 1.0f / sqrtf((float)g.head_k_dim);
   const int mc = (max_len + kL - 1) / kL;
+  p.max_chunks = mc;
   if (g.act_dtype == GDN_BF16) return prefill_d<__bf16>(p, g.head_k_dim, g.conv_kernel, mc, stream);
   return prefill_d<float>(p, g.head_k_dim, g.conv_kernel, mc, stream);
 }

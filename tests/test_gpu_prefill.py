@@ -283,3 +283,18 @@ def test_prefill_without_o_raw(case):
     assert not yh[pad].any()
     untouched = np.setdiff1d(np.arange(rec.shape[0]), live)
     np.testing.assert_array_equal(host(P.rec)[untouched], rec[untouched])
+
+
+@pytest.mark.parametrize("want_o", [True, False])
+def test_prefill_imbalanced_packed_batch(want_o):
+    """Eight packed sequences at Hk=8, Hv=16, d=128 (64-column state tiles)
+    with one much longer than the rest, partial chunks, a one-token
+    sequence, a fresh start and a padding sequence: every head of y (and
+    o_raw), every state and window against the oracle."""
+    s = wl.RANK_LOCAL
+    lens = [1000, 64, 70, 5, 130, 64, 1, 200]
+    w, rec, conv, cu, d = _packed(900, s, lens, 12)
+    slots = np.array([3, 0, 7, 11, -1, 5, 9, 2], np.int32)
+    init = np.array([1, 1, 0, 1, 1, 1, 1, 1], np.uint8)
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="imbalanced packed batch",
+                   want_o=want_o)
