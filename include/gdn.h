@@ -273,6 +273,22 @@ int gdn_state_compact(const gdn_geometry* geom, const gdn_state_pool* pools,
                       const int32_t* dst_host, const int32_t* src_dev,
                       const int32_t* dst_dev, int32_t n, void* stream);
 
+/* ------------------------------------------------------------- checks */
+
+/* Device-side check of a device-resident slot index, for callers that hand
+ * the library slot_idx without a host copy (graph replay): the pages'
+ * engines fail closed on a bad split rather than run with it (pegainfer PR
+ * #1003, PR body, config bullet), and this makes the same rule checkable on
+ * the device.  Enqueues on `stream` (two kernels, capturable in a graph, no
+ * memset) a check of slot_idx [B] against num_slots: every entry negative
+ * (a padding row) or in [0, num_slots), and no non-negative slot named by
+ * two rows.  result: device int32 [2], written by the check:
+ * result[0] = GDN_OK, or GDN_E_SLOT when some row breaks the rule;
+ * result[1] = the smallest such row (a slot out of range, or one that an
+ * earlier row already names), INT32_MAX when none.  B <= 2^20. */
+int gdn_check_slots(const int32_t* slot_idx, int32_t B, int32_t num_slots,
+                    int32_t* result, void* stream);
+
 /* ------------------------------------------------------------- status */
 
 const char* gdn_status_str(int status);

@@ -19,7 +19,7 @@ from ._abi import GDN_BF16, GDN_F32, GdnError
 __all__ = ["Geometry", "LayerWeights", "StatePool", "GdnError", "gdn_slot_bytes",
            "gdn_prefill_scratch_bytes", "gdn_decode_workspace_bytes", "decode_workspace",
            "gdn_conv_update", "gdn_decode_batch",
-           "gdn_decode_step", "gdn_decode_step_noalloc", "gdn_prefill_chunked", "gdn_state_compact", "gdn_linear",
+           "gdn_decode_step", "gdn_decode_step_noalloc", "gdn_prefill_chunked", "gdn_state_compact", "gdn_check_slots", "gdn_linear",
            "library"]
 
 
@@ -265,6 +265,17 @@ def gdn_state_compact(geom: Geometry, pools: list[StatePool], src_host, dst_host
     _abi.check(lib.gdn_state_compact(
         ctypes.byref(g), arr, len(pools), s_hp, d_hp, _ptr(src, torch.int32, n, "src"),
         _ptr(dst, torch.int32, n, "dst"), n, _stream(stream)))
+
+
+def gdn_check_slots(slot_idx: torch.Tensor, num_slots: int, result: torch.Tensor,
+                    stream=None) -> None:
+    """Enqueue the device-side check of slot_idx; result (int32 device [2])
+    receives (status, smallest offending row or INT32_MAX)."""
+    lib = _abi.load()
+    B = slot_idx.numel()
+    _abi.check(lib.gdn_check_slots(_ptr(slot_idx, torch.int32, B, "slot_idx"), B,
+                                   int(num_slots), _ptr(result, torch.int32, 2, "result"),
+                                   _stream(stream)))
 
 
 def _rows(t: torch.Tensor, name: str) -> tuple[int, int, int]:

@@ -84,6 +84,7 @@ PROTOTYPES = {
                                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "gdn_linear": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.POINTER(gdn_linear_out), _I32,
                                   _P]),
+    "gdn_check_slots": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "gdn_state_compact": (ctypes.c_int, [_GP, _PP, _I32, _P, _P, _P, _P, _I32, _P]),
 }
 

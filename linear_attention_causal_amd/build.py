@@ -20,7 +20,7 @@ OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "compact.hip", "linear.hip"]
+SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "compact.hip", "linear.hip", "slots.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

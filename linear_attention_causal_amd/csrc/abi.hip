@@ -300,6 +300,18 @@ int gdn_prefill_chunked(const gdn_geometry* geom, const gdn_layer_weights* w,
                     "gdn_prefill_chunked launch");
 }
 
+int gdn_check_slots(const int32_t* slot_idx, int32_t B, int32_t num_slots, int32_t* result,
+                    void* stream) {
+  if (B < 0 || B > (1 << 20)) return fail(GDN_E_SHAPE, "B = %d outside [0, 2^20]", B);
+  if (num_slots <= 0) return fail(GDN_E_SHAPE, "num_slots must be positive");
+  if (!result || (B > 0 && !slot_idx)) return fail(GDN_E_NULL, "slot_idx or result is NULL");
+  if (reinterpret_cast<uintptr_t>(result) & 3u)
+    return fail(GDN_E_ALIGN, "result must be 4-byte aligned");
+  return hip_status(gdn::launch_check_slots(slot_idx, B, num_slots, result,
+                                            static_cast<hipStream_t>(stream)),
+                    "gdn_check_slots launch");
+}
+
 int gdn_state_compact(const gdn_geometry* geom, const gdn_state_pool* pools, int32_t L,
                       const int32_t* src_host, const int32_t* dst_host,
                       const int32_t* src_dev, const int32_t* dst_dev, int32_t n,

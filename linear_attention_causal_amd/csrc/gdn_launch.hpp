@@ -61,6 +61,11 @@ LinearPlan linear_plan(int M, const LinearOut* outs, int count);
 hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* outs, int count,
                          hipStream_t stream);
 
+// Device-side check of a slot index: result[0] = GDN_OK or GDN_E_SLOT,
+// result[1] = the smallest offending row (INT32_MAX when none).
+hipError_t launch_check_slots(const int32_t* slot, int B, int num_slots, int32_t* result,
+                              hipStream_t stream);
+
 hipError_t launch_compact(const gdn_geometry& g, const gdn_state_pool* pools, int L,
                           const int32_t* src, const int32_t* dst, int n,
                           hipStream_t stream);

@@ -34,7 +34,7 @@ def host_i32(vals):
 
 def test_exports_every_declared_function():
     names = _abi.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(_abi.PROTOTYPES) == set(names)
@@ -254,3 +254,13 @@ def test_linear_validation():
     assert _lin(outs=[(V(0x200000), V(0x300000), 32, 32),
                       (V(0x400000), V(0x300000 + 1000), 32, 32)]) == _abi.GDN_E_OVERLAP
     assert b"overlap" in lib.gdn_last_error()
+
+
+def test_check_slots_validation():
+    """gdn_check_slots rejects bad arguments before any launch."""
+    assert lib.gdn_check_slots(DEV, -1, 64, DEV, None) == _abi.GDN_E_SHAPE
+    assert lib.gdn_check_slots(DEV, (1 << 20) + 1, 64, DEV, None) == _abi.GDN_E_SHAPE
+    assert lib.gdn_check_slots(DEV, 4, 0, DEV, None) == _abi.GDN_E_SHAPE
+    assert lib.gdn_check_slots(None, 4, 64, DEV, None) == _abi.GDN_E_NULL
+    assert lib.gdn_check_slots(DEV, 4, 64, None, None) == _abi.GDN_E_NULL
+    assert lib.gdn_check_slots(DEV, 4, 64, V(0x100002), None) == _abi.GDN_E_ALIGN
