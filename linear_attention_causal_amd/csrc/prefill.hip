@@ -555,12 +555,17 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 // left.  Each kernel keeps under 80 KB of LDS so that two workgroups share a
 // CU and hide each other's latencies.
 
-// One workgroup per (chunk, sequence, K-head).
+// One workgroup per (chunk, sequence, K-head); wave w owns token block w.
+// The conv output passes through one LDS tile twice: first the q rows, which
+// each wave takes into registers as the MFMA A operand of its own token block
+// (16 tokens x D channels), then the k rows, which stay for the transposed
+// k_hat^T reads and the B operands.  One 34 KB tile instead of a q tile
+// beside the k tile leaves room for three workgroups per CU.
 template <typename Act, int D, int K>
-__global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kNT, 3) void prefill_qk_kernel(PrefillParams p) {
   constexpr int LDD = D + 4, NTL = kL / 16, NKS = D / 32;
-  __shared__ __attribute__((aligned(16))) float sQ[kL * LDD];   // q rows (unnormalized)
-  __shared__ __attribute__((aligned(16))) float sK[kL * LDD];   // k rows (unnormalized)
+  static_assert(NTL == kNW, "one token block per wave");
+  __shared__ __attribute__((aligned(16))) float sX[kL * LDD];   // q rows, then k rows (unnormalized)
   __shared__ float sRq[kL], sRk[kL];
 
   int n, c;
@@ -575,65 +580,93 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
   const int li = lane & 15, lk = lane >> 4;
 
   // conv + SiLU of q_m and k_m: thread = (16-byte channel run, run of tokens)
+  constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kNT;
+  static_assert(kNT % G == 0 && TPT >= 1, "q/k conv split");
+  const int grp = tid % G, i_off = (tid / G) * TPT;
+  const int c0 = grp * V;                      // 0 .. 2D-1: q then k
+  const bool isq = c0 < D;
+  const int dcol = isq ? c0 : c0 - D;
+  float out[TPT][V];
   {
-    constexpr int V = 16 / sizeof(Act), G = 2 * D / V, TPT = kL * G / kNT;
-    static_assert(kNT % G == 0 && TPT >= 1, "q/k conv split");
-    const int grp = tid % G, i_off = (tid / G) * TPT;
-    const int c0 = grp * V;                      // 0 .. 2D-1: q then k
-    const int ch = c0 < D ? m * D + c0 : (p.Hk + m) * D + (c0 - D);
-    float* dst = c0 < D ? sQ + c0 : sK + (c0 - D);
-    float out[TPT][V];
+    const int ch = isq ? m * D + c0 : (p.Hk + m) * D + (c0 - D);
     ConvTile<Act, K, TPT> ct;
     ct.fetch(p, si, t0, nc, i_off, ch);
     ct.finish(nc, i_off, out);
+  }
+  auto put = [&]() {
 #pragma unroll
     for (int t = 0; t < TPT; ++t)
 #pragma unroll
       for (int v = 0; v < V; v += 4)
-        *reinterpret_cast<f32x4*>(dst + (i_off + t) * LDD + v) =
+        *reinterpret_cast<f32x4*>(sX + (i_off + t) * LDD + dcol + v) =
             f32x4{out[t][v], out[t][v + 1], out[t][v + 2], out[t][v + 3]};
-  }
+  };
+  // q rows -> A operand of this wave's token block: token 16 wave + li,
+  // channels 32 ks + 8 lk .. +7
+  if (isq) put();
+  __syncthreads();
+  float qa[NKS][8];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sX + (16 * wave + li) * LDD + 32 * ks + 8 * lk + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qa[ks][4 * hf + e] = v[e];
+    }
+  __syncthreads();
+  if (!isq) put();
   __syncthreads();
   // l2 norms as per-row factors (q's includes the 1/sqrt(dk) scale), applied
-  // where the rows are used: PARTS lanes per row
+  // where the rows are used: q over the four lanes of a token, k over PARTS
+  // lanes per row of the tile
   {
+    float sq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = fmaf(qa[ks][e], qa[ks][e], sq);
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    if (lk == 0) sRq[16 * wave + li] = p.scale / sqrtf(sq + p.l2eps);
     constexpr int PARTS = kNT / kL, QD = D / PARTS;
     const int i = tid / PARTS, part = tid % PARTS;
-    float sq = 0.f, sk = 0.f;
+    float sk = 0.f;
 #pragma unroll
     for (int d = part * QD; d < (part + 1) * QD; ++d) {
-      const float qv = sQ[i * LDD + d], kv = sK[i * LDD + d];
-      sq = fmaf(qv, qv, sq);
+      const float kv = sX[i * LDD + d];
       sk = fmaf(kv, kv, sk);
     }
 #pragma unroll
-    for (int off = 1; off < PARTS; off <<= 1) {
-      sq += __shfl_xor(sq, off, 64);
-      sk += __shfl_xor(sk, off, 64);
-    }
-    if (part == 0) {
-      sRq[i] = p.scale / sqrtf(sq + p.l2eps);
-      sRk[i] = 1.0f / sqrtf(sk + p.l2eps);
-    }
+    for (int off = 1; off < PARTS; off <<= 1) sk += __shfl_xor(sk, off, 64);
+    if (part == 0) sRk[i] = 1.0f / sqrtf(sk + p.l2eps);
   }
   __syncthreads();
-  // q_hat rows and k_hat^T as bf16 (hi, lo) fragments
-  for (int u = tid; u < kL * (D / 8); u += kNT) {
-    const int i = u / (D / 8), d0 = 8 * (u - i * (D / 8));
-    float v[8];
+  // q_hat rows as bf16 (hi, lo) fragments, straight from the registers (the
+  // wave's lane is the fragment lane of block (token block, ks)); the raw q
+  // split once for the Q K^T products
+  bf16x8 qh[NKS], ql[NKS];
+  {
+    const float rq = sRq[16 * wave + li];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = sQ[i * LDD + d0 + e] * sRq[i];
-    bf16x8 h, l;
-    split8(v, h, l);
-    const size_t at = frag_at(gk, kL, D, i, d0);
-    *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
-    if (!p.o_bf16) *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;   // (read by 3-pass outputs only)
+    for (int ks = 0; ks < NKS; ++ks) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = qa[ks][e] * rq;
+      bf16x8 h, l;
+      split8(v, h, l);
+      const size_t at = frag_lane(gk * (NTL * NKS) + wave * NKS + ks, lane);
+      *reinterpret_cast<bf16x8*>(p.s.qh[0] + at) = h;
+      if (!p.o_bf16) *reinterpret_cast<bf16x8*>(p.s.qh[1] + at) = l;   // (read by 3-pass outputs only)
+      split8(qa[ks], qh[ks], ql[ks]);
+    }
   }
+  // k_hat^T as bf16 (hi, lo) fragments
   for (int u = tid; u < D * (kL / 8); u += kNT) {
     const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = sK[(i0 + e) * LDD + d] * sRk[i0 + e];
+    for (int e = 0; e < 8; ++e) v[e] = sX[(i0 + e) * LDD + d] * sRk[i0 + e];
     bf16x8 h, l;
     split8(v, h, l);
     const size_t at = frag_at(gk, D, kL, d, i0);
@@ -642,21 +675,23 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
   }
   // K K^T and Q K^T, lower block triangle, 3-pass bf16, rows scaled by the
   // norm factors, out as f32 [64][64] (the strictly upper blocks are not
-  // written; their readers select them away)
+  // written; their readers select them away).  Wave w takes the Q K^T tiles
+  // of its own token block (w + 1 of them) and 4 - w of the K K^T tiles, five
+  // tiles per wave.
   float* gG = p.s.gq + gk * 2 * kL * kL;
-  for (int t = wave; t < 2 * NTL * (NTL + 1) / 2; t += kNW) {
-    const bool isG = t < NTL * (NTL + 1) / 2;
-    int I = 0, rem = isG ? t : t - NTL * (NTL + 1) / 2;
-    while (rem > I) { rem -= I + 1; ++I; }
-    const int J = rem;
-    const float* Asrc = isG ? sK : sQ;
+  auto tile = [&](bool isG, int I, int J) {
     Acc3 acc = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 ah, al, bh, bl;
-      split8(Asrc + (16 * I + li) * LDD + 32 * ks + 8 * lk, ah, al);
-      split8(sK + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
-      mfma3(acc, ah, al, bh, bl);
+      bf16x8 bh, bl;
+      split8(sX + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
+      if (isG) {
+        bf16x8 ah, al;
+        split8(sX + (16 * I + li) * LDD + 32 * ks + 8 * lk, ah, al);
+        mfma3(acc, ah, al, bh, bl);
+      } else {
+        mfma3(acc, qh[ks], ql[ks], bh, bl);
+      }
     }
     const f32x4 r = fold(acc);
     float* dst = gG + (isG ? 0 : kL * kL);
@@ -667,6 +702,13 @@ __global__ __launch_bounds__(kNT) void prefill_qk_kernel(PrefillParams p) {
       const int i = 16 * I + 4 * lk + e;
       dst[i * kL + 16 * J + li] = r[e] * ra[i] * rj;
     }
+  };
+  for (int J = 0; J <= wave; ++J) tile(false, wave, J);
+  const int first = 4 * wave - wave * (wave - 1) / 2;   // K K^T tiles first .. first + 3 - wave
+  for (int t = first; t < first + NTL - wave; ++t) {
+    int I = 0, rem = t;
+    while (rem > I) { rem -= I + 1; ++I; }
+    tile(true, I, rem);
   }
 }
 
