@@ -556,16 +556,24 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 // CU and hide each other's latencies.
 
 // One workgroup per (chunk, sequence, K-head); wave w owns token block w.
-// The conv output passes through one LDS tile twice: first the q rows, which
-// each wave takes into registers as the MFMA A operand of its own token block
-// (16 tokens x D channels), then the k rows, which stay for the transposed
-// k_hat^T reads and the B operands.  One 34 KB tile instead of a q tile
-// beside the k tile leaves room for three workgroups per CU.
+// The conv output passes through one LDS tile: first the q rows, which each
+// wave takes into registers as the MFMA A operand of its own token block (16
+// tokens x D channels), then the k rows (f32) for the norms and the
+// transposed k_hat^T reads, then the same k rows split once into bf16 (hi,
+// lo) planes, from which the K K^T and Q K^T products read their operands
+// directly.  One 35 KB tile instead of a q tile beside the k tile leaves room
+// for three workgroups per CU.
 template <typename Act, int D, int K>
 __global__ __launch_bounds__(kNT, 3) void prefill_qk_kernel(PrefillParams p) {
   constexpr int LDD = D + 4, NTL = kL / 16, NKS = D / 32;
+  constexpr int LDH = D + 8;   // row length of the bf16 planes
+  constexpr int XB = kL * LDD * 4, HB = 2 * kL * LDH * 2;
   static_assert(NTL == kNW, "one token block per wave");
-  __shared__ __attribute__((aligned(16))) float sX[kL * LDD];   // q rows, then k rows (unnormalized)
+  // q rows, then k rows (f32, unnormalized); then the k rows as hi and lo planes
+  __shared__ __attribute__((aligned(16))) unsigned char sBuf[XB > HB ? XB : HB];
+  float* sX = reinterpret_cast<float*>(sBuf);
+  __bf16* sKh = reinterpret_cast<__bf16*>(sBuf);
+  __bf16* sKl = sKh + kL * LDH;
   __shared__ float sRq[kL], sRk[kL];
 
   int n, c;
@@ -661,9 +669,10 @@ __global__ __launch_bounds__(kNT, 3) void prefill_qk_kernel(PrefillParams p) {
       split8(qa[ks], qh[ks], ql[ks]);
     }
   }
-  // k_hat^T as bf16 (hi, lo) fragments
+  // k_hat^T as bf16 (hi, lo) fragments: the lanes of a wave take consecutive
+  // channels d, so the column reads of the tile fall in distinct banks
   for (int u = tid; u < D * (kL / 8); u += kNT) {
-    const int d = u / (kL / 8), i0 = 8 * (u - d * (kL / 8));
+    const int d = u % D, i0 = 8 * (u / D);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = sX[(i0 + e) * LDD + d] * sRk[i0 + e];
@@ -672,6 +681,24 @@ __global__ __launch_bounds__(kNT, 3) void prefill_qk_kernel(PrefillParams p) {
     const size_t at = frag_at(gk, D, kL, d, i0);
     *reinterpret_cast<bf16x8*>(p.s.kt[0] + at) = h;
     *reinterpret_cast<bf16x8*>(p.s.kt[1] + at) = l;
+  }
+  // the raw k rows split once into the hi and lo planes, in place: each
+  // thread takes SH consecutive values of one row, then writes them back split
+  // after every read of the f32 tile is done
+  {
+    constexpr int SH = kL * D / kNT, PER = D / SH;
+    static_assert(SH % 8 == 0 && PER * SH == D, "plane split");
+    const int r = tid / PER, c0 = (tid % PER) * SH;
+    bf16x8 h[SH / 8], l[SH / 8];
+#pragma unroll
+    for (int j = 0; j < SH / 8; ++j) split8(sX + r * LDD + c0 + 8 * j, h[j], l[j]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SH / 8; ++j) {
+      *reinterpret_cast<bf16x8*>(sKh + r * LDH + c0 + 8 * j) = h[j];
+      *reinterpret_cast<bf16x8*>(sKl + r * LDH + c0 + 8 * j) = l[j];
+    }
+    __syncthreads();
   }
   // K K^T and Q K^T, lower block triangle, 3-pass bf16, rows scaled by the
   // norm factors, out as f32 [64][64] (the strictly upper blocks are not
@@ -683,12 +710,11 @@ __global__ __launch_bounds__(kNT, 3) void prefill_qk_kernel(PrefillParams p) {
     Acc3 acc = acc3(f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 bh, bl;
-      split8(sX + (16 * J + li) * LDD + 32 * ks + 8 * lk, bh, bl);
+      const int bo = (16 * J + li) * LDH + 32 * ks + 8 * lk;
+      const bf16x8 bh = ld8(sKh + bo), bl = ld8(sKl + bo);
       if (isG) {
-        bf16x8 ah, al;
-        split8(sX + (16 * I + li) * LDD + 32 * ks + 8 * lk, ah, al);
-        mfma3(acc, ah, al, bh, bl);
+        const int ao = (16 * I + li) * LDH + 32 * ks + 8 * lk;
+        mfma3(acc, ld8(sKh + ao), ld8(sKl + ao), bh, bl);
       } else {
         mfma3(acc, qh[ks], ql[ks], bh, bl);
       }
@@ -1327,19 +1353,10 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   const long long tok0 = si.begin + t0;
   const int tid = threadIdx.x, sub = tid % LPR, rr = tid / LPR;
   const int d0 = sub * VPL;
-  if (si.slot < 0) {  // padding sequence: zero outputs
-    for (int pass = 0; pass < NP; ++pass) {
-      const int i = pass * ROWS + rr;
-      if (i < nc)
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-          const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0 + k;
-          io::store(p.y, o, 0.f);
-          if (!OB) p.obuf[o] = 0.f;   // (the bf16 scratch copy is no output)
-        }
-    }
-    return;
-  }
+  // every load of the chunk first, then the padding test: the slot index's
+  // round trip overlaps them instead of coming before them (the rows of a
+  // padding sequence were never written and are read only to be dropped; the
+  // compiler-only fence keeps the loads above the test)
   f32x4 ov[NP][2], zv[NP][2];
 #pragma unroll
   for (int pass = 0; pass < NP; ++pass) {
@@ -1362,6 +1379,20 @@ __global__ __launch_bounds__(kNT) void prefill_norm_kernel(PrefillParams p) {
   f32x4 nw[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) nw[hf] = *reinterpret_cast<const f32x4*>(p.norm_w + d0 + 4 * hf);
+  asm volatile("" ::: "memory");
+  if (si.slot < 0) {  // padding sequence: zero outputs
+    for (int pass = 0; pass < NP; ++pass) {
+      const int i = pass * ROWS + rr;
+      if (i < nc)
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+          const size_t o = ((size_t)(tok0 + i) * p.Hv + h) * D + d0 + k;
+          io::store(p.y, o, 0.f);
+          if (!OB) p.obuf[o] = 0.f;   // (the bf16 scratch copy is no output)
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int pass = 0; pass < NP; ++pass) {
     const int i = pass * ROWS + rr;
