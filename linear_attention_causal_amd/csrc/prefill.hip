@@ -741,21 +741,25 @@ __global__ __launch_bounds__(kNT, 3) void prefill_qk_kernel(PrefillParams p) {
 // One workgroup per (chunk, V-head).  W's row factor beta_j e^{gamma_j} is
 // split between the two sides of W^T = (K^T diag(e^gamma)) (Tm diag(beta))^T:
 // e^gamma scales the k_hat^T fragments from the q/k kernel in registers, so
-// W and U share the one LDS tile Tm diag(beta), and the kernel's 54 KB of LDS
-// leave room for three workgroups per CU.
+// W and U share the one LDS tile Tm diag(beta).  The v conv is computed
+// straight into the B-operand registers of U (each lane: one channel, eight
+// consecutive tokens), so v never passes through LDS, and the split Tm
+// diag(beta) takes the place of A once the inverse is done: 40 KB of LDS.
 template <typename Act, int D, int K>
 __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int LDL = kL + 4, NTL = kL / 16, NDB = D / 16;
-  constexpr int LDH = kL + 8;   // bf16 row length of the split Tm tiles
-  static_assert(D * LDL <= 2 * kL * LDL, "v^T fits the A | Tm tile");
-  static_assert(4 * 16 * 17 * 4 <= 2 * kL * LDH * 2, "inverse scratch fits the split tile");
-  __shared__ __attribute__((aligned(16))) float sAT[2 * kL * LDL];   // A | Tm, then v^T
-  __shared__ __attribute__((aligned(16))) __bf16 sTb[2][kL * LDH];   // Tm diag(beta)
+  constexpr int LDH = kL + 8;   // bf16 row length of the split Tm tiles (16-byte rows)
+  // region 0 holds A (f32), then the split Tm diag(beta) (bf16 hi, lo);
+  // region 1 holds Tm (f32)
+  constexpr int R0 = kL * LDL * 4 > 2 * kL * LDH * 2 ? kL * LDL * 4 : 2 * kL * LDH * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char sAT[R0 + kL * LDL * 4];
+  __shared__ __attribute__((aligned(16))) float sM[4 * 16 * 17];    // the inverse's staging tiles
   __shared__ float sGam[kL], sBeta[kL], sEg[kL];
-  float* sA = sAT;
-  float* sT = sAT + kL * LDL;
-  float* sVt = sAT;
+  float* sA = reinterpret_cast<float*>(sAT);
+  float* sT = reinterpret_cast<float*>(sAT + R0);
+  __bf16* sTb0 = reinterpret_cast<__bf16*>(sAT);   // Tm diag(beta) hi, lo: in A's place
+  __bf16* sTb1 = sTb0 + kL * LDH;
 
   // Block x -> unit (chunk, K-head) = (x / (8 r)) * 8 + x % 8 and V-head
   // m r + (x / 8) % r: the r workgroups of a unit get ids 8 apart, so they
@@ -814,19 +818,36 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
     alog = p.A_log[h];
     dtb = p.dt_bias[h];
   }
-  // (kL * VG / VTPT threads take part: whole waves, the rest skip it)
-  constexpr int VV = 16 / sizeof(Act), VG = D / VV;
-  constexpr int VTPT = kL * VG >= kNT ? kL * VG / kNT : 1;
-  static_assert(kNT % VG == 0 && (kL * VG / VTPT) % 64 == 0, "v conv split");
-  const bool vact = tid < kL * VG / VTPT;
-  const int vgrp = tid % VG, vi_off = (tid / VG) * VTPT;
-  ConvTile<Act, K, VTPT> vct;
-  if (vact) vct.fetch(p, si, t0, nc, vi_off, 2 * p.Hk * D + h * D + vgrp * VV);
+  // v conv inputs in the B-operand layout of U: for column block db = wave +
+  // kNW it and k-step ks, lane li + 16 lk takes channel 16 db + li at tokens
+  // 32 ks + 8 lk .. +7, i.e. the K - 1 + 8 raw inputs from 32 ks + 8 lk - (K - 1)
+  constexpr int DBW = (NDB + kNW - 1) / kNW;   // column blocks per wave
+  constexpr int VR = 8 + K - 1;                // raw inputs per (block, k-step)
+  typename act_io<Act>::raw_t vraw[DBW][2][VR], vwr[DBW][K];
+  uint32_t vuse[DBW][2];
+#pragma unroll
+  for (int it = 0; it < DBW; ++it) {
+    const int db = min(wave + kNW * it, NDB - 1);
+    const int ch = 2 * p.Hk * D + h * D + 16 * db + li;
+    const ChanReader<Act, K> rd(p, si, ch);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      vuse[it][ks] = 0;
+#pragma unroll
+      for (int j = 0; j < VR; ++j) {
+        const int r = 32 * ks + 8 * lk - (K - 1) + j;   // relative to the chunk start
+        bool u;
+        vraw[it][ks][j] = rd.fetch(t0 + r, r < nc, u);
+        vuse[it][ks] |= (uint32_t)u << j;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) vwr[it][k] = io::load_raw(p.conv_w, (size_t)ch * K + k);
+  }
   // k_hat^T fragments of this wave's W/U column blocks db = wave + kNW it
   // (the A operand of W^T, from the q/k kernel), requested now, after every
   // load the phases before W/U wait for, so their latency passes under the
   // gates, A/P and the inverse
-  constexpr int DBW = (NDB + kNW - 1) / kNW;   // column blocks per wave
   bf16x8 kth[DBW][2], ktl[DBW][2];
 #pragma unroll
   for (int it = 0; it < DBW; ++it) {
@@ -876,11 +897,31 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
     *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
     if (!p.o_bf16) *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;   // (read by 3-pass outputs only)
   }
-  float vout[VTPT][VV];
-  if (vact) vct.finish(nc, vi_off, vout);   // held until A and Tm are dead
+  // v conv + SiLU (tokens at or past nc give zero), held as U's B operand
+  float vo[DBW][2][8];
+#pragma unroll
+  for (int it = 0; it < DBW; ++it) {
+    float w[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[k] = io::from_raw(vwr[it][k]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float xs[VR];
+#pragma unroll
+      for (int j = 0; j < VR; ++j)
+        xs[j] = (vuse[it][ks] >> j) & 1u ? io::from_raw(vraw[it][ks][j]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc = fmaf(w[k], xs[e + k], acc);
+        vo[it][ks][e] = 32 * ks + 8 * lk + e < nc ? silu_fast(acc) : 0.f;
+      }
+    }
+  }
   __syncthreads();
-  // (the inverse stages its blocks in sTb and ends with a barrier)
-  unit_lower_inverse<LDL>(sA, sT, reinterpret_cast<float*>(&sTb[0][0]), tid);
+  // (the inverse ends with a barrier)
+  unit_lower_inverse<LDL>(sA, sT, sM, tid);
   // Tm diag(beta), split (strictly upper blocks zero)
   for (int u = tid; u < kL * (kL / 8); u += kNT) {
     const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
@@ -890,15 +931,9 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
     for (int e = 0; e < 8; ++e) vb[e] = upper ? 0.f : sT[i * LDL + j0 + e] * sBeta[j0 + e];
     bf16x8 h8, l8;
     split8(vb, h8, l8);
-    *reinterpret_cast<bf16x8*>(&sTb[0][i * LDH + j0]) = h8;
-    *reinterpret_cast<bf16x8*>(&sTb[1][i * LDH + j0]) = l8;
+    *reinterpret_cast<bf16x8*>(sTb0 + i * LDH + j0) = h8;
+    *reinterpret_cast<bf16x8*>(sTb1 + i * LDH + j0) = l8;
   }
-  __syncthreads();  // A and Tm (f32) are dead: v^T goes in their place
-  if (vact)
-#pragma unroll
-    for (int v = 0; v < VV; ++v)
-#pragma unroll
-      for (int t = 0; t < VTPT; ++t) sVt[(vgrp * VV + v) * LDL + vi_off + t] = vout[t][v];
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < DBW; ++it) {
@@ -916,15 +951,10 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
         kv[e] = ((float)kth[it][ks][e] + (float)ktl[it][ks][e]) * sEg[32 * ks + 8 * lk + e];
       split8(kv, kh[ks], kl[ks]);
     }
-    // v^T rows d, split (B operand of U)
+    // v of channel d at the lane's tokens, split (B operand of U)
     bf16x8 vh[2], vl[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float vv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vv[e] = sVt[d * LDL + 32 * ks + 8 * lk + e];
-      split8(vv, vh[ks], vl[ks]);
-    }
+    for (int ks = 0; ks < 2; ++ks) split8(vo[it][ks], vh[ks], vl[ks]);
 #pragma unroll
     for (int tb = 0; tb < NTL; ++tb) {
       // rows 16 tb + li of Tm diag(beta): B operand of W^T and A operand of U
@@ -932,8 +962,8 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int o = (16 * tb + li) * LDH + 32 * ks + 8 * lk;
-        bh[ks] = ld8(&sTb[0][o]);
-        bl[ks] = ld8(&sTb[1][o]);
+        bh[ks] = ld8(sTb0 + o);
+        bl[ks] = ld8(sTb1 + o);
       }
       Acc3 aw = acc3(f32x4{0.f, 0.f, 0.f, 0.f});   // W^T: rows d, columns token
       Acc3 au = acc3(f32x4{0.f, 0.f, 0.f, 0.f});   // U: rows token, columns d
