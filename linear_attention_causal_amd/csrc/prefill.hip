@@ -552,8 +552,8 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 //   P = lower(e^{gamma_i - gamma_j} q_i.k_j)
 //   W = Tm diag(beta e^gamma) K,  U = Tm diag(beta) V
 // so that the sequential pass only has V' = U - W S and the state update
-// left.  Each kernel keeps under 80 KB of LDS so that two workgroups share a
-// CU and hide each other's latencies.
+// left.  Both keep their LDS near 40 KB and their registers under 170 so
+// that three workgroups share a CU and hide each other's latencies.
 
 // One workgroup per (chunk, sequence, K-head); wave w owns token block w.
 // The conv output passes through one LDS tile: first the q rows, which each
