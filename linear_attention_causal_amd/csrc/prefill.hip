@@ -156,6 +156,9 @@ struct PrefillParams {
   bool inl;
   int32_t inl_cu[kInlineSeqs + 1];
   int32_t inl_cb[kInlineSeqs + 1];
+  // the state pass's sequence order, longest first: its workgroups are
+  // dispatched in this order, so the longest chain of chunks starts first
+  int32_t inl_order[kInlineSeqs];
   int N, Hk, Hv, C, num_slots, r;
   int max_chunks;       // chunks of the longest sequence
   float l2eps, rmseps, scale;
@@ -1047,7 +1050,8 @@ __global__ __launch_bounds__(state_threads<NCB>()) void prefill_state_kernel(Pre
   const int grp = blockIdx.x / (8 * per), rem = blockIdx.x - grp * 8 * per;
   const int unit = grp * 8 + (rem & 7), k = rem >> 3;
   if (unit >= p.N * p.Hk) return;
-  const int n = unit / p.Hk, m = unit - n * p.Hk;
+  const int nu = unit / p.Hk, m = unit - nu * p.Hk;
+  const int n = p.inl ? p.inl_order[nu] : nu;
   const int h = m * p.r + k / tiles, col0 = (k % tiles) * DVT;
   const SeqInfo si = seq_info(p, n);
   if (si.slot < 0) return;
@@ -1551,6 +1555,16 @@ hipError_t launch_prefill(const gdn_geometry& g, const gdn_layer_weights& w,
       p.inl_cu[n] = cu_seqlens_host[n];
       p.inl_cb[n] = run;
       if (n < N) run += (cu_seqlens_host[n + 1] - cu_seqlens_host[n] + kL - 1) / kL;
+    }
+    // longest first, ties in batch order (insertion sort: at most 64 entries)
+    for (int n = 0; n < N; ++n) {
+      const int len = cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+      int at = n;
+      while (at > 0 && cu_seqlens_host[p.inl_order[at - 1] + 1] - cu_seqlens_host[p.inl_order[at - 1]] < len) {
+        p.inl_order[at] = p.inl_order[at - 1];
+        --at;
+      }
+      p.inl_order[at] = n;
     }
   }
   p.obuf = o_raw ? o_raw : p.s.o;
