@@ -298,3 +298,39 @@ def test_prefill_imbalanced_packed_batch(want_o):
     init = np.array([1, 1, 0, 1, 1, 1, 1, 1], np.uint8)
     _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag="imbalanced packed batch",
                    want_o=want_o)
+
+
+@pytest.mark.parametrize("want_o", [True, False])
+def test_prefill_sequence_order_invariance(want_o):
+    """Each sequence of a packed batch is computed on its own (its chunks
+    never span another's, and the state pass takes the sequences longest
+    first whatever their order): the same sequences packed in reverse order,
+    with their slots and flags, give bit-identical y (and o_raw), states and
+    conv windows.  64-column state tiles (Hk=8, Hv=16, d=128, eight
+    sequences)."""
+    s = wl.RANK_LOCAL
+    lens = [1000, 64, 70, 5, 130, 64, 1, 200]
+    w, rec, conv, cu, d = _packed(950, s, lens, 12)
+    slots = np.array([3, 0, 7, 11, -1, 5, 9, 2], np.int32)
+    init = np.array([1, 1, 0, 1, 1, 1, 1, 1], np.uint8)
+    L = Layer(s, w)
+    rev = np.arange(len(lens))[::-1]
+    lens_r = [lens[n] for n in rev]
+    cu_r = np.concatenate([[0], np.cumsum(lens_r)]).astype(np.int32)
+    tok_r = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in rev]).astype(np.int64)
+    d_r = {k: d[k][tok_r] for k in ("x", "z", "a", "b")}
+    runs = []
+    for order, (c, sl, hi, dd) in enumerate(((cu, slots, init, d), (cu_r, slots[rev], init[rev], d_r))):
+        print(f"[prefill] order invariance, packing {order} o_raw={want_o}", flush=True)
+        P = Pool(s, rec, conv)
+        y, o = prefill(L, P, c, sl, dd["x"], dd["z"], dd["a"], dd["b"], has_init=hi,
+                       want_o=want_o)
+        torch.cuda.synchronize()
+        runs.append((host(y), host(o) if want_o else None, host(P.rec), host(P.conv)))
+    (y0, o0, r0, c0), (y1, o1, r1, c1) = runs
+    # row t of the reversed packing holds row tok_r[t] of the original one
+    np.testing.assert_array_equal(y1, y0[tok_r])
+    if want_o:
+        np.testing.assert_array_equal(o1, o0[tok_r])
+    np.testing.assert_array_equal(r1, r0)
+    np.testing.assert_array_equal(c1, c0)
