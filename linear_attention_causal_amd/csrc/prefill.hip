@@ -752,6 +752,7 @@ template <typename Act, int D, int K>
 __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
   using io = act_io<Act>;
   constexpr int LDL = kL + 4, NTL = kL / 16, NDB = D / 16;
+  constexpr int DBW = (NDB + kNW - 1) / kNW;   // column blocks per wave
   constexpr int LDH = kL + 8;   // bf16 row length of the split Tm tiles (16-byte rows)
   // region 0 holds A (f32), then the split Tm diag(beta) (bf16 hi, lo);
   // region 1 holds Tm (f32)
@@ -793,8 +794,8 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
 
-  // K K^T and Q K^T rows of this thread's A/P runs, the gate inputs (wave 0)
-  // and the v conv inputs are all requested first
+  // K K^T and Q K^T rows of this thread's A/P runs and the gate inputs
+  // (wave 0) are requested first
   constexpr int APR = kL * (kL / 8) / kNT;   // A/P runs per thread
   static_assert(kL * (kL / 8) % kNT == 0, "A/P split");
   const float* gG = p.s.gq + gk * 2 * kL * kL;
@@ -820,47 +821,6 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
     b_in = io::load(p.b, (size_t)tk * p.Hv + h);
     alog = p.A_log[h];
     dtb = p.dt_bias[h];
-  }
-  // v conv inputs in the B-operand layout of U: for column block db = wave +
-  // kNW it and k-step ks, lane li + 16 lk takes channel 16 db + li at tokens
-  // 32 ks + 8 lk .. +7, i.e. the K - 1 + 8 raw inputs from 32 ks + 8 lk - (K - 1)
-  constexpr int DBW = (NDB + kNW - 1) / kNW;   // column blocks per wave
-  constexpr int VR = 8 + K - 1;                // raw inputs per (block, k-step)
-  typename act_io<Act>::raw_t vraw[DBW][2][VR], vwr[DBW][K];
-  uint32_t vuse[DBW][2];
-#pragma unroll
-  for (int it = 0; it < DBW; ++it) {
-    const int db = min(wave + kNW * it, NDB - 1);
-    const int ch = 2 * p.Hk * D + h * D + 16 * db + li;
-    const ChanReader<Act, K> rd(p, si, ch);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      vuse[it][ks] = 0;
-#pragma unroll
-      for (int j = 0; j < VR; ++j) {
-        const int r = 32 * ks + 8 * lk - (K - 1) + j;   // relative to the chunk start
-        bool u;
-        vraw[it][ks][j] = rd.fetch(t0 + r, r < nc, u);
-        vuse[it][ks] |= (uint32_t)u << j;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) vwr[it][k] = io::load_raw(p.conv_w, (size_t)ch * K + k);
-  }
-  // k_hat^T fragments of this wave's W/U column blocks db = wave + kNW it
-  // (the A operand of W^T, from the q/k kernel), requested now, after every
-  // load the phases before W/U wait for, so their latency passes under the
-  // gates, A/P and the inverse
-  bf16x8 kth[DBW][2], ktl[DBW][2];
-#pragma unroll
-  for (int it = 0; it < DBW; ++it) {
-    const int db = min(wave + kNW * it, NDB - 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const size_t at = frag_lane((gk * NDB + db) * 2 + ks, lane);
-      kth[it][ks] = ld8(p.s.kt[0] + at);
-      ktl[it][ks] = ld8(p.s.kt[1] + at);
-    }
   }
   // gates: running sum gamma, beta, and e^gamma (the K side of W's factor)
   if (wave == 0) {
@@ -900,6 +860,50 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
     *reinterpret_cast<bf16x8*>(p.s.pm[0] + at) = h8;
     if (!p.o_bf16) *reinterpret_cast<bf16x8*>(p.s.pm[1] + at) = l8;   // (read by 3-pass outputs only)
   }
+  // v conv inputs in the B-operand layout of U: for column block db = wave +
+  // kNW it and k-step ks, lane li + 16 lk takes channel 16 db + li at tokens
+  // 32 ks + 8 lk .. +7, i.e. the K - 1 + 8 raw inputs from 32 ks + 8 lk - (K - 1)
+  constexpr int VR = 8 + K - 1;                // raw inputs per (block, k-step)
+  typename act_io<Act>::raw_t vraw[DBW][2][VR], vwr[DBW][K];
+  uint32_t vuse[DBW][2];
+#pragma unroll
+  for (int it = 0; it < DBW; ++it) {
+    const int db = min(wave + kNW * it, NDB - 1);
+    const int ch = 2 * p.Hk * D + h * D + 16 * db + li;
+    const ChanReader<Act, K> rd(p, si, ch);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      vuse[it][ks] = 0;
+#pragma unroll
+      for (int j = 0; j < VR; ++j) {
+        const int r = 32 * ks + 8 * lk - (K - 1) + j;   // relative to the chunk start
+        bool u;
+        vraw[it][ks][j] = rd.fetch(t0 + r, r < nc, u);
+        vuse[it][ks] |= (uint32_t)u << j;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) vwr[it][k] = io::load_raw(p.conv_w, (size_t)ch * K + k);
+  }
+  // k_hat^T fragments of this wave's W/U column blocks db = wave + kNW it
+  // (the A operand of W^T, from the q/k kernel).  These and the v conv
+  // inputs above are requested only here, once A and P are formed, so their
+  // latency passes under the inverse and their registers are not held
+  // beside the K K^T / Q K^T rows (148 registers instead of 168)
+  bf16x8 kth[DBW][2], ktl[DBW][2];
+#pragma unroll
+  for (int it = 0; it < DBW; ++it) {
+    const int db = min(wave + kNW * it, NDB - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const size_t at = frag_lane((gk * NDB + db) * 2 + ks, lane);
+      kth[it][ks] = ld8(p.s.kt[0] + at);
+      ktl[it][ks] = ld8(p.s.kt[1] + at);
+    }
+  }
+  __syncthreads();
+  // (the inverse ends with a barrier)
+  unit_lower_inverse<LDL>(sA, sT, sM, tid);
   // v conv + SiLU (tokens at or past nc give zero), held as U's B operand
   float vo[DBW][2][8];
 #pragma unroll
@@ -922,9 +926,6 @@ __global__ __launch_bounds__(kNT, 3) void prefill_wy_kernel(PrefillParams p) {
       }
     }
   }
-  __syncthreads();
-  // (the inverse ends with a barrier)
-  unit_lower_inverse<LDL>(sA, sT, sM, tid);
   // Tm diag(beta), split (strictly upper blocks zero)
   for (int u = tid; u < kL * (kL / 8); u += kNT) {
     const int i = u / (kL / 8), j0 = 8 * (u - i * (kL / 8));
