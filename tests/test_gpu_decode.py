@@ -161,7 +161,9 @@ def test_decode_repeated_steps_match_oracle():
                                    (wl.Shape(4, 16, 64, 64, 3, "bf16"), 40, 50),
                                    (wl.Shape(4, 4, 64, 64, 2, "bf16"), 6, 8),
                                    (wl.Shape(2, 6, 32, 32, 4, "f32"), 4, 7),
-                                   (wl.Shape(2, 6, 32, 32, 4, "f32"), 180, 200)])
+                                   (wl.Shape(2, 6, 32, 32, 4, "f32"), 180, 200),
+                                   (wl.Shape(2, 4, 64, 64, 4, "f32"), 9, 12),
+                                   (wl.Shape(2, 4, 128, 128, 3, "f32"), 9, 12)])
 def test_fused_decode_step_matches_oracle_and_two_calls(s, B, P):
     """gdn_decode_step (conv + state step + gated norm in one launch) against
     the oracle, and against gdn_conv_update + gdn_decode_batch on a copy of

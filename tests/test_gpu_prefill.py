@@ -88,6 +88,19 @@ def test_prefill_ragged_single(T):
     _check_prefill(s, w, rec, conv, cu, np.array([1], np.int32), d, tag=f"f32 d32 T={T}")
 
 
+@pytest.mark.parametrize("D,K", [(64, 4), (128, 3)])
+def test_prefill_packed_f32_wide_heads(D, K):
+    """f32 activations at head dims 64 and 128 (16-byte runs of four
+    channels in the conv tiles): packed sequences with partial chunks, a
+    one-token sequence, a fresh start and a padding sequence."""
+    s = wl.Shape(2, 4, D, D, K, "f32")
+    lens = [70, 130, 1, 64, 17]
+    slots = np.array([3, 0, 5, -1, 1], np.int32)
+    init = np.array([1, 1, 1, 1, 0], np.uint8)
+    w, rec, conv, cu, d = _packed(400 + D + K, s, lens, 7)
+    _check_prefill(s, w, rec, conv, cu, slots, d, has_init=init, tag=f"packed f32 d{D} K={K}")
+
+
 @pytest.mark.parametrize("want_o", [True, False])
 def test_prefill_packed_mixed_bf16(want_o):
     """Packed sequences with a zero-length one, a fresh start (has_init = 0),
