@@ -10,7 +10,7 @@
 //
 // Two kernels, chosen by the row count M:
 //   stream (M <= 32, decode): a weight stream, each weight byte used by at
-//     most 32 rows.  A workgroup owns 16 or 32 output columns; its four
+//     most 32 rows.  A workgroup owns 8, 16 or 32 output columns; its four
 //     waves split K and request every weight and input fragment of their K
 //     range before the first MFMA, and add their partial tiles through LDS.
 //   tile (M > 32): a dense product.  A workgroup owns a BM x BN output tile
@@ -74,13 +74,18 @@ __device__ __forceinline__ void store_tile(const LinearOut& o, int M, int m0, in
   }
 }
 
-template <int MT, int NT, int KW>
+// CW: the workgroup's output columns when NT == 1 and they are fewer than 16
+// (the B operand's upper eight rows then repeat the last column and their
+// results are not stored), so that a weight of few columns still spreads
+// over every CU.
+template <int MT, int NT, int KW, int CW = 16 * NT>
 __global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
+  static_assert(CW == 16 * NT || (NT == 1 && CW < 16), "column split");
   constexpr int KB = MT + NT <= 3 ? 16 : 8;  // k-steps requested at once
   __shared__ f32x4 s_part[KW][MT * NT][64];
   const int g = group_of(p, blockIdx.x);
   const LinearOut o = p.out[g];
-  const int n0 = ((int)blockIdx.x - o.tile0) * 16 * NT, mb = blockIdx.y * 16 * MT;
+  const int n0 = ((int)blockIdx.x - o.tile0) * CW, mb = blockIdx.y * 16 * MT;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int li = lane & 15, lk = lane >> 4;
   const int ksteps = (p.K + 31) / 32;
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
 #pragma unroll
   for (int t = 0; t < MT; ++t) xr[t] = p.x + (size_t)min(mb + 16 * t + li, p.M - 1) * p.ldx;
 #pragma unroll
-  for (int u = 0; u < NT; ++u) wr[u] = o.w + (size_t)min(n0 + 16 * u + li, o.N - 1) * p.K;
+  for (int u = 0; u < NT; ++u) wr[u] = o.w + (size_t)min(n0 + 16 * u + min(li, CW - 1), o.N - 1) * p.K;
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -135,7 +140,8 @@ __global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
     f32x4 s = s_part[0][i][lane];
 #pragma unroll
     for (int w = 1; w < KW; ++w) s += s_part[w][i][lane];
-    store_tile(o, p.M, mb + 16 * (i / NT), n0 + 16 * (i % NT), lane, s);
+    if (CW >= 16 || (lane & 15) < CW)
+      store_tile(o, p.M, mb + 16 * (i / NT), n0 + 16 * (i % NT), lane, s);
   }
 }
 
@@ -294,8 +300,10 @@ LinearPlan linear_plan(int M, const LinearOut* outs, int count) {
   }
   if (M <= 32) {
     // two column tiles per workgroup once single tiles would fill the chip
-    // (halves the input-row reads per weight byte)
-    const int cols = cols16 >= 256 ? 32 : 16;
+    // (halves the input-row reads per weight byte); for up to 16 rows, half
+    // tiles while single ones would not (out_proj of 16 rows at N = 2048:
+    // 6.1 -> 5.6 us)
+    const int cols = cols16 >= 256 ? 32 : (M <= 16 ? 8 : 16);
     return {LinearPlan::kStream, M <= 16 ? 16 : 32, cols};
   }
   // the largest tile that still gives at least 128 workgroups
@@ -317,6 +325,8 @@ hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* 
   p.count = count;
   const LinearPlan plan = linear_plan(M, outs, count);
   if (plan.kind == LinearPlan::kStream) {
+    if (plan.rows == 16 && plan.cols == 8)
+      return launch(linear_stream_kernel<1, 1, 4, 8>, p, outs, 8, 16, 256, stream);
     if (plan.rows == 16 && plan.cols == 16)
       return launch(linear_stream_kernel<1, 1, 4>, p, outs, 16, 16, 256, stream);
     if (plan.rows == 16) return launch(linear_stream_kernel<1, 2, 4>, p, outs, 32, 16, 256, stream);
