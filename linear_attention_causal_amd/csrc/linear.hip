@@ -15,10 +15,11 @@
 //     range before the first MFMA, and add their partial tiles through LDS.
 //   tile (M > 32): a dense product.  A workgroup owns a BM x BN output tile
 //     (128 x 128 with eight waves or 128 x 64 with four, the larger that
-//     still gives 128 workgroups, else 64 x 32 with two); x and w tiles of 32 k-columns are staged through three
-//     LDS buffers in MFMA fragment order, so each wave reads its operands
+//     still gives 128 workgroups, else 64 x 32 with two); x and w tiles are
+//     staged, one or two 32-wide k-steps per barrier, through three LDS
+//     buffers in MFMA fragment order, so each wave reads its operands
 //     with linear 16-byte LDS reads, and the input rows are fetched once
-//     per BN columns instead of once per 16.  Global loads run eight
+//     per BN columns instead of once per 16.  Global loads run six or eight
 //     k-steps ahead in registers.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -149,27 +150,30 @@ __global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
 // The 128 x 128 tile runs eight waves (two per SIMD, so one wave's LDS and
 // barrier waits overlap the other's MFMAs); with four, each wave's registers
 // allow only one wave per SIMD.
-// Global loads run D k-steps ahead of the MFMAs through a ring of D
-// register stages; each k-step is copied into one of three LDS buffers two
-// steps before its MFMAs, and its fragments are read from LDS one step
-// before, so LDS latency hides behind the previous step's MFMAs.
-template <int BM, int BN, int D, int NW>
+// K is taken in stages of KS k-steps of 32.  Global loads run DS stages
+// ahead of the MFMAs through a ring of DS register stages; each stage is
+// copied into one of three LDS buffers two stages before its MFMAs, and its
+// fragments are read from LDS one stage before, so LDS latency hides behind
+// the previous stage's MFMAs.  One barrier per stage: KS k-steps of MFMAs
+// between barriers.
+template <int BM, int BN, int KS, int DS, int NW>
 __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
-  static_assert(D >= 3, "the ring holds the two k-steps ahead of the LDS copy");
+  static_assert(DS >= 3, "the ring holds the two stages ahead of the LDS copy");
   constexpr int NTH = 64 * NW;                      // threads
   constexpr int WNW = NW / 2;                       // waves along n (two along m)
   constexpr int TM = BM / 32, TN = BN / (16 * WNW); // 16 x 16 tiles per wave
   constexpr int XP = 4 * BM / NTH, WP = 4 * BN / NTH; // 16-byte pieces per thread per k-step
   static_assert(TN >= 1 && XP >= 1 && WP >= 1, "tile shape");
-  // one k-step of each operand in fragment order: [16-row tile][lane] x 16 bytes
-  __shared__ lbf16x8 xs[3][BM / 16][64];
-  __shared__ lbf16x8 ws[3][BN / 16][64];
+  // one stage of each operand in fragment order: [k-step][16-row tile][lane] x 16 bytes
+  __shared__ lbf16x8 xs[3][KS][BM / 16][64];
+  __shared__ lbf16x8 ws[3][KS][BN / 16][64];
   const int g = group_of(p, blockIdx.x);
   const LinearOut o = p.out[g];
   const int n0 = ((int)blockIdx.x - o.tile0) * BN, m0 = blockIdx.y * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WNW, wn = wave % WNW;
   const int ksteps = (p.K + 31) / 32;
+  const int nst = (ksteps + KS - 1) / KS;           // stages
   // piece q = tid + NTH i: tile row r = q / 4, k-chunk c = q % 4 (the same c
   // for every piece of a thread); its LDS slot is fragment r / 16, lane
   // r % 16 + 16 c.  Rows past M or N are clamped (read, never stored); a
@@ -192,30 +196,39 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
     wsrc[i] = o.w + (size_t)min(n0 + r, o.N - 1) * p.K;
     wslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
   }
-  lbf16x8 xr[D][XP], wr[D][WP];
-  const auto fetch = [&](int st, int ks) {
-    const int k = 32 * ks + 8 * c;
-    const int off = k < p.K ? k : 0;
+  lbf16x8 xr[DS][KS][XP], wr[DS][KS][WP];
+  const auto fetch = [&](int st, int S) {
 #pragma unroll
-    for (int i = 0; i < XP; ++i) xr[st][i] = raw8(xsrc[i] + off);
+    for (int kk = 0; kk < KS; ++kk) {
+      const int k = 32 * (KS * S + kk) + 8 * c;
+      const int off = k < p.K ? k : 0;
 #pragma unroll
-    for (int i = 0; i < WP; ++i) wr[st][i] = raw8(wsrc[i] + off);
+      for (int i = 0; i < XP; ++i) xr[st][kk][i] = raw8(xsrc[i] + off);
+#pragma unroll
+      for (int i = 0; i < WP; ++i) wr[st][kk][i] = raw8(wsrc[i] + off);
+    }
   };
   const auto put = [&](int st, int buf) {
 #pragma unroll
-    for (int i = 0; i < XP; ++i) (&xs[buf][0][0])[xslot[i]] = xr[st][i];
+    for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-    for (int i = 0; i < WP; ++i) (&ws[buf][0][0])[wslot[i]] = wr[st][i];
+      for (int i = 0; i < XP; ++i) (&xs[buf][kk][0][0])[xslot[i]] = xr[st][kk][i];
+#pragma unroll
+      for (int i = 0; i < WP; ++i) (&ws[buf][kk][0][0])[wslot[i]] = wr[st][kk][i];
+    }
   };
-  // the k-step holding the end of K, when K is not a multiple of 32
-  const int tail = (p.K & 31) ? ksteps - 1 : -1;
-  const bool lane_in = 32 * tail + 8 * (lane >> 4) < p.K;
-  lbf16x8 fa[TM], fb[TN];
-  const auto frags = [&](int buf, lbf16x8* a, lbf16x8* b) {
+  // the last stage, when it holds the end of K inside a k-step or k-steps
+  // past K (its lanes past K are zeroed)
+  const int last = (p.K == 32 * KS * nst) ? -1 : nst - 1;
+  lbf16x8 fa[KS][TM], fb[KS][TN];
+  const auto frags = [&](int buf, lbf16x8 (*a)[TM], lbf16x8 (*b)[TN]) {
 #pragma unroll
-    for (int t = 0; t < TM; ++t) a[t] = xs[buf][wm * TM + t][lane];
+    for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-    for (int u = 0; u < TN; ++u) b[u] = ws[buf][wn * TN + u][lane];
+      for (int t = 0; t < TM; ++t) a[kk][t] = xs[buf][kk][wm * TM + t][lane];
+#pragma unroll
+      for (int u = 0; u < TN; ++u) b[kk][u] = ws[buf][kk][wn * TN + u][lane];
+    }
   };
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -223,51 +236,60 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
 #pragma unroll
     for (int u = 0; u < TN; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int d = 0; d < D; ++d) fetch(d, d);
+  for (int d = 0; d < DS; ++d) fetch(d, d);
   put(0, 0);
   put(1, 1);
   __syncthreads();
   frags(0, fa, fb);
-  // Step ks: read k-step ks + 1's fragments (LDS buffer (ks + 1) % 3),
-  // MFMAs of k-step ks, copy k-step ks + 2 (ring stage (ks + 2) % D) into
-  // buffer (ks + 2) % 3, whose fragments were read two barriers ago, and
-  // fetch k-step ks + D into stage ks % D, copied to LDS two steps ago.
-  // Loads and copies always run (steps past K read row starts); in the
-  // guarded form the MFMAs of steps past K are skipped and the lanes of the
-  // K tail are zeroed.  The main loop takes only whole groups of D steps
-  // that lie inside K, so it has no branches for the scheduler to stop at.
-  const auto step = [&](int d, int ks, bool guarded) {
-    lbf16x8 na[TM], nb[TN];
-    frags((ks + 1) % 3, na, nb);
-    if (guarded && ks == tail) {
+  // Stage S: read stage S + 1's fragments (LDS buffer (S + 1) % 3), MFMAs of
+  // stage S, copy stage S + 2 (ring slot (S + 2) % DS) into buffer (S + 2) %
+  // 3, whose fragments were read two barriers ago, and fetch stage S + DS
+  // into slot S % DS, copied to LDS two stages ago.  Loads and copies always
+  // run (stages past K read row starts); in the guarded form the MFMAs of
+  // stages past K are skipped and the lanes past K are zeroed.  The main loop
+  // takes only whole groups of DS stages that lie inside K, so it has no
+  // branches for the scheduler to stop at.
+  const auto step = [&](int d, int S, bool guarded) {
+    lbf16x8 na[KS][TM], nb[KS][TN];
+    frags((S + 1) % 3, na, nb);
+    if (guarded && S == last) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t) fa[t] = keep(fa[t], lane_in);
+      for (int kk = 0; kk < KS; ++kk) {
+        const bool in = 32 * (KS * S + kk) + 8 * (lane >> 4) < p.K;
 #pragma unroll
-      for (int u = 0; u < TN; ++u) fb[u] = keep(fb[u], lane_in);
+        for (int t = 0; t < TM; ++t) fa[kk][t] = keep(fa[kk][t], in);
+#pragma unroll
+        for (int u = 0; u < TN; ++u) fb[kk][u] = keep(fb[kk][u], in);
+      }
     }
-    if (!guarded || ks < ksteps) {
+    if (!guarded || S < nst) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t)
+      for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int u = 0; u < TN; ++u) acc[t][u] = mfma16(fa[t], fb[u], acc[t][u]);
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+          for (int u = 0; u < TN; ++u) acc[t][u] = mfma16(fa[kk][t], fb[kk][u], acc[t][u]);
     }
-    put((d + 2) % D, (ks + 2) % 3);
-    fetch(d, ks + D);
+    put((d + 2) % DS, (S + 2) % 3);
+    fetch(d, S + DS);
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < TM; ++t) fa[t] = na[t];
+    for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-    for (int u = 0; u < TN; ++u) fb[u] = nb[u];
+      for (int t = 0; t < TM; ++t) fa[kk][t] = na[kk][t];
+#pragma unroll
+      for (int u = 0; u < TN; ++u) fb[kk][u] = nb[kk][u];
+    }
   };
-  const int kfull = tail >= 0 ? tail : ksteps;  // steps without a K tail
-  int ks0 = 0;
-  for (; ks0 + D <= kfull; ks0 += D) {
+  const int sfull = last >= 0 ? last : nst;  // stages without a K end inside
+  int s0 = 0;
+  for (; s0 + DS <= sfull; s0 += DS) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) step(d, ks0 + d, false);
+    for (int d = 0; d < DS; ++d) step(d, s0 + d, false);
   }
-  for (; ks0 < ksteps; ks0 += D) {
+  for (; s0 < nst; s0 += DS) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) step(d, ks0 + d, true);
+    for (int d = 0; d < DS; ++d) step(d, s0 + d, true);
   }
 #pragma unroll
   for (int t = 0; t < TM; ++t)
@@ -334,10 +356,10 @@ hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* 
     return launch(linear_stream_kernel<2, 2, 4>, p, outs, 32, 32, 256, stream);
   }
   if (plan.rows == 128 && plan.cols == 128)
-    return launch(linear_tile_kernel<128, 128, 8, 8>, p, outs, 128, 128, 512, stream);
+    return launch(linear_tile_kernel<128, 128, 2, 3, 8>, p, outs, 128, 128, 512, stream);
   if (plan.rows == 128)
-    return launch(linear_tile_kernel<128, 64, 8, 4>, p, outs, 64, 128, 256, stream);
-  return launch(linear_tile_kernel<64, 32, 8, 2>, p, outs, 32, 64, 128, stream);
+    return launch(linear_tile_kernel<128, 64, 1, 8, 4>, p, outs, 64, 128, 256, stream);
+  return launch(linear_tile_kernel<64, 32, 1, 8, 2>, p, outs, 32, 64, 128, stream);
 }
 
 }  // namespace gdn
