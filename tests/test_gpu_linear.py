@@ -57,6 +57,8 @@ def _run_linear(M, K, Ns, seed, x_pad=0, y_pad=0):
     (130, 72, [200, 5]),                  # tiled, partial row block and K tail
     (512, 1024, [1024]),                  # tiled, large tile
     (300, 200, [16000, 7]),               # 128 x 128 tile: partial row tile, K tail, ragged N
+    (300, 232, [16000, 7]),               # 128 x 128 tile: K ends in a stage's second k-step
+    (260, 96, [16384]),                   # 128 x 128 tile: fewer k-step stages than loads ahead
 ])
 def test_linear(M, K, Ns):
     _run_linear(M, K, Ns, seed=M + K)
