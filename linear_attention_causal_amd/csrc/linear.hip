@@ -15,7 +15,8 @@
 //     range before the first MFMA, and add their partial tiles through LDS.
 //   tile (M > 32): a dense product.  A workgroup owns a BM x BN output tile
 //     (128 x 128 with eight waves or 128 x 64 with four, the larger that
-//     still gives 128 workgroups, else 64 x 32 with two); x and w tiles are
+//     still gives 128 workgroups, else 64 x 32 with two waves on each half
+//     of K, four in all); x and w tiles are
 //     staged, one or two 32-wide k-steps per barrier, through three LDS
 //     buffers in MFMA fragment order, so each wave reads its operands
 //     with linear 16-byte LDS reads, and the input rows are fetched once
@@ -156,24 +157,39 @@ __global__ __launch_bounds__(64 * KW) void linear_stream_kernel(LinParams p) {
 // fragments are read from LDS one stage before, so LDS latency hides behind
 // the previous stage's MFMAs.  One barrier per stage: KS k-steps of MFMAs
 // between barriers.
-template <int BM, int BN, int KS, int DS, int NW>
-__global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
+// KG > 1 splits K inside the workgroup: KG groups of NW waves each take a
+// contiguous share of the k-steps through their own LDS buffers, in the same
+// stages and barriers, and group 0 adds the others' tiles at the end.  A
+// small tile then keeps every SIMD of its CU busy.
+template <int BM, int BN, int KS, int DS, int NW, int KG = 1>
+__global__ __launch_bounds__(64 * NW * KG) void linear_tile_kernel(LinParams p) {
   static_assert(DS >= 3, "the ring holds the two stages ahead of the LDS copy");
-  constexpr int NTH = 64 * NW;                      // threads
+  constexpr int NTH = 64 * NW;                      // threads of one k-group
   constexpr int WNW = NW / 2;                       // waves along n (two along m)
   constexpr int TM = BM / 32, TN = BN / (16 * WNW); // 16 x 16 tiles per wave
   constexpr int XP = 4 * BM / NTH, WP = 4 * BN / NTH; // 16-byte pieces per thread per k-step
   static_assert(TN >= 1 && XP >= 1 && WP >= 1, "tile shape");
   // one stage of each operand in fragment order: [k-step][16-row tile][lane] x 16 bytes
-  __shared__ lbf16x8 xs[3][KS][BM / 16][64];
-  __shared__ lbf16x8 ws[3][KS][BN / 16][64];
+  __shared__ lbf16x8 xsg[KG][3][KS][BM / 16][64];
+  __shared__ lbf16x8 wsg[KG][3][KS][BN / 16][64];
   const int g = group_of(p, blockIdx.x);
   const LinearOut o = p.out[g];
   const int n0 = ((int)blockIdx.x - o.tile0) * BN, m0 = blockIdx.y * BM;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, kg = wave_id() / NW, wave = wave_id() - kg * NW;
+  const int tid = threadIdx.x - kg * NTH;           // thread within the k-group
   const int wm = wave / WNW, wn = wave % WNW;
-  const int ksteps = (p.K + 31) / 32;
-  const int nst = (ksteps + KS - 1) / KS;           // stages
+  auto& xs = xsg[kg];
+  auto& ws = wsg[kg];
+  // this group's k-steps: [kg * kspg, (kg + 1) * kspg) of the whole, as a
+  // product of depth Kg from column k0 on (every group runs the stages of
+  // the largest share; a group past its own skips their MFMAs)
+  const int kspg = ((p.K + 31) / 32 + KG - 1) / KG;
+  const int k0 = min(p.K, 32 * kspg * kg);
+  const int Kg = min(p.K, 32 * kspg * (kg + 1)) - k0;
+  const int ksteps = (Kg + 31) / 32;
+  const int nst = (ksteps + KS - 1) / KS;           // this group's stages
+  const int nall = (kspg + KS - 1) / KS;            // stages every group runs
+  const int kb = Kg > 0 ? k0 : 0;   // a group with no k-steps reads row starts only
   // piece q = tid + NTH i: tile row r = q / 4, k-chunk c = q % 4 (the same c
   // for every piece of a thread); its LDS slot is fragment r / 16, lane
   // r % 16 + 16 c.  Rows past M or N are clamped (read, never stored); a
@@ -187,13 +203,13 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int r = (tid + NTH * i) >> 2;
-    xsrc[i] = p.x + (size_t)min(m0 + r, p.M - 1) * p.ldx;
+    xsrc[i] = p.x + (size_t)min(m0 + r, p.M - 1) * p.ldx + kb;
     xslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
   }
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
     const int r = (tid + NTH * i) >> 2;
-    wsrc[i] = o.w + (size_t)min(n0 + r, o.N - 1) * p.K;
+    wsrc[i] = o.w + (size_t)min(n0 + r, o.N - 1) * p.K + kb;
     wslot[i] = (r >> 4) * 64 + (r & 15) + 16 * c;
   }
   lbf16x8 xr[DS][KS][XP], wr[DS][KS][WP];
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int k = 32 * (KS * S + kk) + 8 * c;
-      const int off = k < p.K ? k : 0;
+      const int off = k < Kg ? k : 0;
 #pragma unroll
       for (int i = 0; i < XP; ++i) xr[st][kk][i] = raw8(xsrc[i] + off);
 #pragma unroll
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
   };
   // the last stage, when it holds the end of K inside a k-step or k-steps
   // past K (its lanes past K are zeroed)
-  const int last = (p.K == 32 * KS * nst) ? -1 : nst - 1;
+  const int last = (Kg == 32 * KS * nst) ? -1 : nst - 1;
   lbf16x8 fa[KS][TM], fb[KS][TN];
   const auto frags = [&](int buf, lbf16x8 (*a)[TM], lbf16x8 (*b)[TN]) {
 #pragma unroll
@@ -255,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
     if (guarded && S == last) {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const bool in = 32 * (KS * S + kk) + 8 * (lane >> 4) < p.K;
+        const bool in = 32 * (KS * S + kk) + 8 * (lane >> 4) < Kg;
 #pragma unroll
         for (int t = 0; t < TM; ++t) fa[kk][t] = keep(fa[kk][t], in);
 #pragma unroll
@@ -281,15 +297,44 @@ __global__ __launch_bounds__(64 * NW) void linear_tile_kernel(LinParams p) {
       for (int u = 0; u < TN; ++u) fb[kk][u] = nb[kk][u];
     }
   };
-  const int sfull = last >= 0 ? last : nst;  // stages without a K end inside
+  // stages without a K end inside, in every group (the loop bounds are the
+  // same for all waves: they meet at every barrier)
+  int sfull = nall;
+#pragma unroll
+  for (int q = 0; q < KG; ++q) {
+    const int kq = min(p.K, 32 * kspg * (q + 1)) - min(p.K, 32 * kspg * q);
+    const int nq = (kq + 32 * KS - 1) / (32 * KS);
+    sfull = min(sfull, kq == 32 * KS * nq ? nq : nq - 1);
+  }
   int s0 = 0;
   for (; s0 + DS <= sfull; s0 += DS) {
 #pragma unroll
     for (int d = 0; d < DS; ++d) step(d, s0 + d, false);
   }
-  for (; s0 < nst; s0 += DS) {
+  for (; s0 < nall; s0 += DS) {
 #pragma unroll
     for (int d = 0; d < DS; ++d) step(d, s0 + d, true);
+  }
+  if constexpr (KG > 1) {
+    // the other groups' tiles through LDS (the operand buffers are free
+    // after the last barrier), added by group 0
+    static_assert(sizeof(xsg) >= (size_t)(KG - 1) * NTH * TM * TN * sizeof(f32x4), "reduce space");
+    f32x4* red = reinterpret_cast<f32x4*>(&xsg[0][0][0][0][0]);
+    if (kg > 0)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+          red[(((kg - 1) * NW + wave) * TM * TN + t * TN + u) * 64 + lane] = acc[t][u];
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int q = 1; q < KG; ++q)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+          acc[t][u] += red[(((q - 1) * NW + wave) * TM * TN + t * TN + u) * 64 + lane];
   }
 #pragma unroll
   for (int t = 0; t < TM; ++t)
@@ -332,8 +377,8 @@ LinearPlan linear_plan(int M, const LinearOut* outs, int count) {
   const long long rows128 = (M + 127) / 128;
   if (cols128 * rows128 >= 128) return {LinearPlan::kTile, 128, 128};
   if (cols64 * rows128 >= 128) return {LinearPlan::kTile, 128, 64};
-  // otherwise 64 x 32 tiles of two waves: twice the workgroups of 64 x 64
-  // tiles, so the product spreads over twice the CUs
+  // otherwise 64 x 32 tiles (two waves on each half of K): twice the
+  // workgroups of 64 x 64 tiles, so the product spreads over twice the CUs
   return {LinearPlan::kTile, 64, 32};
 }
 
@@ -359,7 +404,7 @@ hipError_t launch_linear(const void* x, int M, int K, int ldx, const LinearOut* 
     return launch(linear_tile_kernel<128, 128, 2, 3, 8>, p, outs, 128, 128, 512, stream);
   if (plan.rows == 128)
     return launch(linear_tile_kernel<128, 64, 1, 8, 4>, p, outs, 64, 128, 256, stream);
-  return launch(linear_tile_kernel<64, 32, 1, 8, 2>, p, outs, 32, 64, 128, stream);
+  return launch(linear_tile_kernel<64, 32, 1, 8, 2, 2>, p, outs, 32, 64, 256, stream);
 }
 
 }  // namespace gdn
